@@ -1,0 +1,28 @@
+"""Float64 CPU oracle for exact scaled dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or call anything in this package.  The product path (the HIP library
+and its Python binding in ``exact_tiled_attention_13_amd``) never imports,
+calls or links it, and this package imports nothing from the product.
+
+Contents
+--------
+``attention``        plain definition, O = softmax(scale*Q K^T + mask) V, with
+                     causal (bottom-right), key-padding and GQA semantics.
+``attention_rows``   the same definition evaluated one (b, h, i) row at a time,
+                     for sampled checks at sizes the dense form cannot reach.
+``decode``           one new query per sequence against a contiguous KV cache.
+``tiled_attention``  the tile-by-tile online-softmax algorithm (running max and
+                     denominator, earlier partials rescaled), step by step.
+
+Parity status: every function above is pinned by tests/test_oracle_pins.py
+(closed forms, invariants, a textbook library routine and brute force on tiny
+inputs).  No page prints output values for the seeded workloads, so the
+seeded outputs themselves are pinned only through those properties.
+"""
+
+from .attention import attention, attention_rows, decode, valid_lengths
+from .tiled import tiled_attention
+
+__all__ = ["attention", "attention_rows", "decode", "valid_lengths", "tiled_attention"]
