@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal|long|ragged|decode|single]
+
+A step is one pass of the hot path over one batch of synthetic, seeded input
+already resident in HBM.  The headline line measures the causal prefill
+workload (B=4, H=16, T=1024, D=64, bf16) in TFLOP/s of algorithmic work
+(4*D flops per unmasked (query, key) pair); the same run also times one
+KV-cache decode step of the GQA decode workload (B=64, Hq=32, Hkv=8, D=128,
+lengths 1024..32768) in GB/s of algorithmic bytes (the K/V rows each sequence
+needs plus q, o, lse and lengths), reported under "decode".  Steps are
+replayed from a HIP graph (a fixed number of calls per graph) so that host
+launch overhead does not enter the timing; the kernels are timed with HIP
+events recorded on the stream they run on.
+
+The float64 CPU oracle is timed on a bounded sample of the same workload
+(cpu_baseline).  It is a reported baseline, not the target.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU * 2.4 GHz * 4096 dense bf16 flop/clk/CU
+PEAK_F32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+CALLS_PER_GRAPH = 20
+
+
+def prefill_pairs(B, Hq, Tq, Tk, causal, lens):
+    """Number of unmasked (query, key) pairs, summed over batch and heads."""
+    total = 0
+    for b in range(B):
+        lk = Tk if lens is None else int(min(max(lens[b], 0), Tk))
+        lq = lk if (lens is not None and Tq == Tk) else Tq
+        off = lk - lq
+        i = np.arange(lq, dtype=np.int64)
+        seen = np.clip(np.minimum(lk, i + off + 1), 0, None) if causal else np.full(lq, lk, dtype=np.int64)
+        total += int(seen.sum())
+    return total * Hq
+
+
+def decode_bytes(W, lens, elem=2):
+    kv = 2 * W.Hkv * W.D * elem * int(np.sum(np.clip(lens, 0, W.Tk)))
+    return kv + 2 * W.B * W.Hq * W.D * elem + W.B * W.Hq * 4 + W.B * 4
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class Graphed:
+    """A HIP graph holding CALLS_PER_GRAPH calls of fn, replayed to run steps."""
+
+    def __init__(self, torch, fn):
+        self.torch = torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()  # eager call on the capture stream before capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            for _ in range(CALLS_PER_GRAPH):
+                fn()
+        torch.cuda.synchronize()
+
+    def run(self, steps):
+        for _ in range(max(1, steps // CALLS_PER_GRAPH)):
+            self.g.replay()
+
+
+def time_steps(torch, runner, steps, warmup):
+    """Warm up, then time exactly `steps` steps (rounded to whole graphs)."""
+    runner.run(warmup)
+    torch.cuda.synchronize()
+    n = max(1, steps // CALLS_PER_GRAPH) * CALLS_PER_GRAPH
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    runner.run(n)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    return ev0.elapsed_time(ev1) / n, wall_ms / n, n
+
+
+def setup_prefill(torch, name):
+    import exact_tiled_attention_13_amd as ea
+    from exact_tiled_attention_13_amd import workloads
+
+    w = workloads.make(name, device="cpu")
+    W = w["workload"]
+    q, k, v = (w[x].cuda() for x in ("q", "k", "v"))
+    kv = None if w["kv_lens"] is None else w["kv_lens"].cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((W.B, W.Hq, W.Tq), dtype=torch.float32, device="cuda")
+    dt = ea.MIATTN_BF16 if W.dtype == "bf16" else ea.MIATTN_F32
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq, W.Hkv, W.Tq, W.Tk,
+            W.D, W.scale, int(W.causal), 0 if kv is None else kv.data_ptr(), dt)
+
+    def step():
+        ea.attn_fwd(*args, torch.cuda.current_stream().cuda_stream)
+
+    pairs = prefill_pairs(W.B, W.Hq, W.Tq, W.Tk, W.causal, w["lens"])
+    flops = 4 * W.D * pairs
+    elem = 2 if W.dtype == "bf16" else 4
+    io_bytes = (2 * q.numel() + k.numel() + v.numel()) * elem + lse.numel() * 4
+    keep = (q, k, v, kv, o, lse)
+    return dict(w=w, W=W, step=step, flops=flops, io_bytes=io_bytes, keep=keep, out=(o, lse))
+
+
+def setup_decode(torch):
+    import exact_tiled_attention_13_amd as ea
+    from exact_tiled_attention_13_amd import workloads
+
+    w = workloads.make("decode", device="cuda")
+    W = w["workload"]
+    q, k, v, kv = w["q"], w["k"], w["v"], w["kv_lens"]
+    o = torch.empty_like(q)
+    lse = torch.empty((W.B, W.Hq), dtype=torch.float32, device="cuda")
+    nbytes = ea.attn_decode_workspace_size(W.B, W.Hq, W.Hkv, W.Tk, W.D)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq, W.Hkv, W.Tk, W.D,
+            W.scale, kv.data_ptr(), ws.data_ptr(), nbytes, ea.MIATTN_BF16)
+
+    def step():
+        ea.attn_decode(*args, torch.cuda.current_stream().cuda_stream)
+
+    return dict(w=w, W=W, step=step, bytes=decode_bytes(W, w["lens"]), keep=(q, k, v, kv, o, lse, ws),
+                out=(o, lse))
+
+
+def check_graph_replay(torch, runner, step, out):
+    """Graph replays must reproduce an eager call bit for bit."""
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in out]
+    for _ in range(2):
+        for t in out:
+            t.fill_(0)
+        runner.g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, out):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from the eager call")
+
+
+def cpu_baseline_prefill(name, budget_s):
+    import oracle
+    from exact_tiled_attention_13_amd import workloads
+
+    w = workloads.make(name, device="cpu")
+    W = w["workload"]
+    q, k, v = w["q"], w["k"], w["v"]
+    G = W.Hq // W.Hkv
+    done_flops, heads = 0, 0
+    t0 = time.perf_counter()
+    for b in range(W.B):
+        for h in range(W.Hq):
+            lens = None if w["lens"] is None else w["lens"][b:b + 1]
+            oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1], v[b:b + 1, h // G:h // G + 1],
+                             W.scale, W.causal, lens)
+            done_flops += 4 * W.D * prefill_pairs(1, 1, W.Tq, W.Tk, W.causal, lens)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done_flops / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"{heads} of {W.B * W.Hq} (batch, head) pairs of the {W.name} workload, float64 numpy, "
+                       f"{dt:.1f} s")
+
+
+def cpu_baseline_decode(dec, budget_s):
+    import oracle
+
+    w, W = dec["w"], dec["W"]
+    lens = w["lens"]
+    qc = w["q"].cpu()
+    done, nb = 0, 0
+    t0 = time.perf_counter()
+    for b in range(W.B):
+        oracle.decode(qc, w["k"], w["v"], lens, W.scale, batches=[b])
+        done += 2 * W.Hkv * W.D * 2 * int(lens[b]) + 2 * W.Hq * W.D * 2 + W.Hq * 4 + 4
+        nb += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle",
+                sample=f"{nb} of {W.B} sequences of the decode workload (cache slabs upcast to float64), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="causal", choices=["causal", "long", "ragged", "decode", "single"])
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement of the default run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_tiled_attention_13_amd as ea
+
+    ea.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    line = {}
+    if args.workload == "decode":
+        dec = setup_decode(torch)
+        runner = Graphed(torch, dec["step"])
+        check_graph_replay(torch, runner, dec["step"], dec["out"])
+        ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
+        gbs = dec["bytes"] / (ms * 1e-3) / 1e9
+        W = dec["W"]
+        line = dict(metric="decode KV GB/s (% HBM peak)", value=round(gbs, 2), unit="GB/s", n_gpus=1, steps=n,
+                    warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak",
+                    vs_baseline=None, dtype="bf16", data="synthetic",
+                    config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
+                                sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU"),
+                    roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                                  frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                                  kernels="decode_split + decode_merge"))
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
+        print(json.dumps(line), flush=True)
+        return
+
+    pre = setup_prefill(torch, args.workload)
+    runner = Graphed(torch, pre["step"])
+    check_graph_replay(torch, runner, pre["step"], pre["out"])
+    ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
+    W = pre["W"]
+    tflops = pre["flops"] / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if W.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    line = dict(
+        metric="prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
+        value=round(tflops, 3), unit="TFLOP/s", n_gpus=1, steps=n, warmup=args.warmup,
+        ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype=W.dtype, data="synthetic",
+        config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk, D=W.D, causal=W.causal,
+                    flops_per_step=pre["flops"], parallelism="single GPU"),
+        roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=peak, unit="TFLOP/s",
+                      frac=round(tflops / peak, 4), traffic=None, kernel="fwd_bf16_kernel" if W.dtype == "bf16"
+                      else "fwd_f32_kernel", kernel_ms=round(ms, 5)),
+    )
+    del pre, runner
+    if args.workload == "causal" and not args.no_decode:
+        torch.cuda.empty_cache()
+        dec = setup_decode(torch)
+        drun = Graphed(torch, dec["step"])
+        check_graph_replay(torch, drun, dec["step"], dec["out"])
+        dms, dwall, dn = time_steps(torch, drun, max(20, args.steps // 4), max(5, args.warmup // 4))
+        gbs = dec["bytes"] / (dms * 1e-3) / 1e9
+        DW = dec["W"]
+        line["decode"] = dict(workload=DW.note, value=round(gbs, 2), unit="GB/s", steps=dn, ms_per_step=round(dms, 5),
+                              bytes_per_step=dec["bytes"], sum_lengths=int(np.sum(dec["w"]["lens"])),
+                              roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                                            frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                                            kernels="decode_split + decode_merge"))
+        if not args.no_cpu_baseline:
+            line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget / 2)
+        del dec, drun
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(args.workload, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,132 @@
-"""MI355X-native exact tiled attention (placeholder; binding added with the C ABI)."""
+"""Exact tiled attention for AMD Instinct MI355X (gfx950).
+
+The compute path is the HIP library ``libmiattn.so`` (C ABI in
+``include/miattn.h``); this package is its thin binding.  PyTorch is used for
+device memory and the current stream only.
+
+    o, lse = fwd(q, k, v, causal=True)                 # prefill
+    o, lse = decode(q, k_cache, v_cache, kv_lens)      # one KV-cache decode step
+
+The C-ABI functions are re-exported under their C names (``attn_fwd``,
+``attn_decode``, ``attn_decode_workspace_size``, ``attn_strerror``).
+"""
+
+from __future__ import annotations
+
+import math
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    MIATTN_BF16,
+    MIATTN_F32,
+    MiattnError,
+    attn_abi_version,
+    attn_decode,
+    attn_decode_workspace_size,
+    attn_fwd,
+    attn_strerror,
+    load,
+)
+
+__all__ = ["fwd", "decode", "attn_fwd", "attn_decode", "attn_decode_workspace_size", "attn_strerror",
+           "MiattnError", "load"]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MIATTN_BF16
+    if t.dtype == torch.float32:
+        return MIATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check_tensor(name, t, ndim, dtype, device):
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU device of q ({device}), got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (call .contiguous())")
+
+
+def _lens(kv_lens, B, device, required):
+    torch = _torch()
+    if kv_lens is None:
+        if required:
+            raise ValueError("kv_lens is required")
+        return None
+    if not isinstance(kv_lens, torch.Tensor):
+        kv_lens = torch.as_tensor(kv_lens, dtype=torch.int32)
+    if kv_lens.dtype != torch.int32:
+        raise ValueError("kv_lens must be int32")
+    if kv_lens.shape != (B,):
+        raise ValueError(f"kv_lens must have shape ({B},)")
+    if kv_lens.device != device:
+        raise ValueError("kv_lens must live on the same GPU as q")
+    return kv_lens.contiguous()
+
+
+def fwd(q, k, v, *, causal: bool = False, kv_lens=None, scale: float | None = None, out=None, lse=None):
+    """Prefill attention.  q (B,Hq,Tq,D), k/v (B,Hkv,Tk,D), bf16 or fp32, on the GPU.
+
+    Returns (o (B,Hq,Tq,D) of q's dtype, lse (B,Hq,Tq) float32).
+    """
+    torch = _torch()
+    dt = _dtype_code(q)
+    B, Hq, Tq, D = q.shape
+    _check_tensor("q", q, 4, q.dtype, q.device)
+    _check_tensor("k", k, 4, q.dtype, q.device)
+    _check_tensor("v", v, 4, q.dtype, q.device)
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, Tk = k.shape[1], k.shape[2]
+    lens = _lens(kv_lens, B, q.device, False)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty_like(q) if out is None else out
+    l_out = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv, Tq, Tk, D,
+             scale, 1 if causal else 0, 0 if lens is None else lens.data_ptr(), dt, stream)
+    return o, l_out
+
+
+def decode(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, workspace=None, out=None, lse=None):
+    """One decode step.  q (B,Hq,D), caches (B,Hkv,S_max,D), kv_lens int32 (B,) on the GPU.
+
+    kv_lens[b] counts the valid cached keys including the new token.
+    Returns (o (B,Hq,D), lse (B,Hq) float32).
+    """
+    torch = _torch()
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    _check_tensor("q", q, 3, q.dtype, q.device)
+    _check_tensor("k_cache", k_cache, 4, q.dtype, q.device)
+    _check_tensor("v_cache", v_cache, 4, q.dtype, q.device)
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    lens = _lens(kv_lens, B, q.device, True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = attn_decode_workspace_size(B, Hq, Hkv, S_max, D)
+    if workspace is None and dt == MIATTN_BF16:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv,
+                S_max, D, scale, lens.data_ptr(), ws_ptr, ws_bytes, dt, stream)
+    return o, l_out

@@ -1,0 +1,86 @@
+// C ABI of the attention library: argument checks, kernel selection and
+// error reporting.  Every check runs before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+
+#include "../../include/miattn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_hip_msg[256] = "no HIP error recorded";
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_hip_msg, sizeof(g_hip_msg), "HIP error %d: %s", (int)e, hipGetErrorString(e));
+  return MIATTN_ERR_HIP;
+}
+
+bool supported_d(int D) { return D == 64 || D == 128; }
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return 1; }
+
+const char* attn_strerror(int code) {
+  switch (code) {
+    case MIATTN_OK: return "ok";
+    case MIATTN_ERR_NULL: return "a required pointer is NULL";
+    case MIATTN_ERR_SHAPE: return "bad shape or scale (sizes must be > 0, Hq % Hkv == 0, scale finite)";
+    case MIATTN_ERR_UNSUPPORTED: return "unsupported argument (D must be 64 or 128, dtype 0/1, causal 0/1)";
+    case MIATTN_ERR_WORKSPACE: return "decode workspace missing or smaller than attn_decode_workspace_size()";
+    case MIATTN_ERR_HIP: return g_hip_msg;
+    default: return "unknown error code";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Tq,
+             int Tk, int D, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
+    return MIATTN_ERR_SHAPE;
+  if (!supported_d(D) || (dtype != MIATTN_F32 && dtype != MIATTN_BF16) || (causal != 0 && causal != 1))
+    return MIATTN_ERR_UNSUPPORTED;
+  // one workgroup per 128 query rows per (batch, head) must fit a 1-D grid
+  if ((long long)((Tq + 127) / 128) * B * Hq > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
+  miattn::FwdArgs a{q, k, v, o, lse, kv_lens, B, Hq, Hkv, Tq, Tk, D, scale, causal};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = dtype == MIATTN_BF16 ? miattn::launch_fwd_bf16(a, st) : miattn::launch_fwd_f32(a, st);
+  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0) return 0;
+  return miattn::decode_ws_floats(B, Hq, S_max, D) * sizeof(float);
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+                int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
+    return MIATTN_ERR_SHAPE;
+  if (!supported_d(D) || (dtype != MIATTN_F32 && dtype != MIATTN_BF16)) return MIATTN_ERR_UNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == MIATTN_F32) {
+    // one query row against the cache, bottom-right causal: exactly the decode step
+    if ((long long)B * Hq > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
+    miattn::FwdArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, 1, S_max, D, scale, 1};
+    hipError_t e = miattn::launch_fwd_f32(a, st);
+    return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+  }
+  const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
+  if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
+  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
+  float* ws = static_cast<float*>(workspace);
+  const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
+  miattn::DecodeArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D};
+  hipError_t e = miattn::launch_decode_bf16(a, st);
+  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal launchers behind the C ABI (include/miattn.h).  Arguments are
+// validated by the ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace miattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;              // may be null
+  const int32_t* kv_lens;  // device int32[B] or null
+  int B, Hq, Hkv, Tq, Tk, D;
+  float scale;
+  int causal;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* o;
+  float* lse;              // may be null
+  const int32_t* kv_lens;  // device int32[B], required
+  int B, Hq, Hkv, S_max, D;
+  float scale;
+  float* ws_o;             // split partial outputs
+  float* ws_ml;            // split partial (max, sum)
+};
+
+// Keys handled by one decode split (one wave).
+constexpr int kDecodeSplitKeys = 256;
+
+inline int decode_num_splits(int S_max) { return (S_max + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
+inline size_t decode_ws_floats(int B, int Hq, int S_max, int D) {
+  return (size_t)B * Hq * decode_num_splits(S_max) * (size_t)(D + 2);
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace miattn

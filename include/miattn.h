@@ -1,0 +1,116 @@
+/*
+ * miattn — exact tiled attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Plain device pointers and sizes; no framework types.
+ *
+ * Operation (prefill): O = softmax(scale * Q K^T + mask) V, computed tile by
+ * tile with the online softmax (a running row maximum and denominator; the
+ * earlier partial output is rescaled by exp(m_old - m_new) when the maximum
+ * grows), so the score matrix is never formed in memory.  Sources, by page:
+ *   - "Implementing attention from scratch" (chorfi.xyz), sections Shapes
+ *     first (layouts), Why scale by sqrt(D), Masks, Stable softmax, KV caching
+ *     (decode, bottom-right causal alignment, grouped-query attention) and
+ *     Cost model (decode reads the whole cache);
+ *   - "FlashAttention", Transformers in Action section 9.4.1 and Figure 9.8
+ *     (exact result, tiles streamed through on-chip memory).
+ *
+ * Layouts (all row-major, contiguous, head dim fastest; element type given
+ * by `dtype`):
+ *   q      [B, Hq,  Tq, D]        k, v   [B, Hkv, Tk, D]
+ *   o      [B, Hq,  Tq, D]        lse    [B, Hq,  Tq]       (float32)
+ *   decode: q [B, Hq, D], k_cache / v_cache [B, Hkv, S_max, D],
+ *           o [B, Hq, D], lse [B, Hq]
+ * Query head h uses KV head h / (Hq / Hkv) (consecutive query heads share a
+ * KV head); Hq must be a multiple of Hkv.
+ *
+ * Masks.  kv_lens is a DEVICE int32[B] array or NULL.  Sequence b has
+ * Lk = clamp(kv_lens[b], 0, Tk) valid keys (NULL: Lk = Tk).  If kv_lens is
+ * given and Tq == Tk, the first Lk query rows are valid (self-attention with
+ * padding), else all Tq rows are.  Causal: row i sees keys j <= i + Lk - Lq
+ * (aligned bottom-right).  A row that is padding or sees no key gets
+ * O = 0 and LSE = -inf; no NaN is ever produced.  K/V rows at or past Lk are
+ * never read into the result (they may hold anything, NaN included).
+ *
+ * LSE is the natural-log log-sum-exp of the row's scaled scores over the
+ * keys it sees: lse_i = ln sum_j exp(scale * q_i . k_j).
+ *
+ * Numerics: bf16 inputs are multiplied on the matrix cores with fp32
+ * accumulation; softmax statistics and the output accumulator are fp32; the
+ * probabilities are rounded to bf16 (round to nearest even) for the P V
+ * product and O is rounded to bf16 on store.  fp32 inputs use fp32 matrix
+ * instructions end to end.
+ *
+ * Ownership and concurrency.  The caller owns every buffer (device memory on
+ * the current device).  Inputs are read-only; o must not alias q, k or v.
+ * The library allocates and frees nothing, never synchronises, and launches
+ * on `stream` (a hipStream_t; NULL = the default stream); calls return as
+ * soon as the work is queued.  Functions are thread-safe.
+ *
+ * Errors.  Return 0 on success or a negative MIATTN_ERR_* code.  Arguments
+ * are checked before any HIP call; a failed check launches nothing.  Errors
+ * never abort the process.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MIATTN_F32 = 0,  /* float32 q/k/v/o */
+  MIATTN_BF16 = 1  /* bfloat16 q/k/v/o */
+};
+
+enum {
+  MIATTN_OK = 0,
+  MIATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+  MIATTN_ERR_SHAPE = -2,       /* size <= 0, Hq % Hkv != 0, non-finite scale, or grid too large */
+  MIATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, causal not 0/1 */
+  MIATTN_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  MIATTN_ERR_HIP = -5          /* the HIP runtime refused a launch; see attn_strerror */
+};
+
+/*
+ * Prefill attention.  q, k, v, o: device pointers of `dtype` elements in the
+ * layouts above.  lse: device float32 [B, Hq, Tq] or NULL (not written).
+ * scale: any finite value (1/sqrt(D) is the usual one).  causal: 0 or 1.
+ * kv_lens: device int32[B] or NULL.  D must be 64 or 128.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+             const int32_t* kv_lens, int dtype, void* stream);
+
+/* Bytes of device workspace attn_decode needs for these sizes (bf16 path). */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int D);
+
+/*
+ * One decode step: one new query per (sequence, query head) against a
+ * contiguous per-layer KV cache.  kv_lens (device int32[B], required) counts
+ * the valid cached keys of each sequence INCLUDING the new token, whose K/V
+ * the caller has already written at index kv_lens[b]-1; the query sees keys
+ * 0 .. kv_lens[b]-1.  lse: device float32 [B, Hq] or NULL.  workspace:
+ * device memory of at least attn_decode_workspace_size(...) bytes, used for
+ * split partial results; contents on entry do not matter.  For dtype
+ * MIATTN_F32 the workspace is not used and may be NULL.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                int B, int Hq, int Hkv, int S_max, int D, float scale,
+                const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
+                int dtype, void* stream);
+
+/* Static text for a return code; for MIATTN_ERR_HIP, the last HIP error seen
+ * by the calling thread. */
+const char* attn_strerror(int code);
+
+/* Library ABI version (incremented on incompatible changes). */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */

@@ -1,0 +1,104 @@
+"""Host-side tests of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU.
+
+Only calls whose arguments fail validation are made here, so nothing is ever
+launched (these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_13_amd as ea
+from exact_tiled_attention_13_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmiattn.so is not built; run `python -m exact_tiled_attention_13_amd.build`")
+    return _lib.load()
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_abi_version(lib):
+    assert ea.attn_abi_version() == 1
+
+
+def test_strerror_covers_codes(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        assert ea.attn_strerror(code)
+    assert "unknown" in ea.attn_strerror(-99)
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,code", [
+    # q, k, v, o null
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1),
+    # sizes
+    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Tq=0), -2), (dict(Tk=-1), -2),
+    (dict(Hq=6, Hkv=4), -2), (dict(scale=float("nan")), -2), (dict(scale=float("inf")), -2),
+    (dict(D=0), -2),
+    # unsupported
+    (dict(D=96), -3), (dict(D=256), -3), (dict(dtype=2), -3), (dict(causal=2), -3),
+])
+def test_fwd_validation(lib, args, code):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=0, B=1, Hq=2, Hkv=1, Tq=8, Tk=8, D=64, scale=0.125,
+             causal=0, kv_lens=0, dtype=1, stream=0)
+    a.update(args)
+    assert ea.attn_fwd(**a, check=False) == code
+    with pytest.raises(ea.MiattnError) as e:
+        ea.attn_fwd(**a)
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(kv_lens=0), -1), (dict(q=0), -1), (dict(k_cache=0), -1),
+    (dict(S_max=0), -2), (dict(Hq=5, Hkv=2), -2), (dict(scale=float("nan")), -2),
+    (dict(D=32), -3), (dict(dtype=7), -3),
+    (dict(workspace=0), -4), (dict(workspace_bytes=10), -4),
+])
+def test_decode_validation(lib, args, code):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, S_max=100, D=128, scale=0.1,
+             kv_lens=FAKE, workspace=FAKE, workspace_bytes=1 << 40, dtype=1, stream=0)
+    a.update(args)
+    assert ea.attn_decode(**a, check=False) == code
+
+
+def test_workspace_size(lib):
+    # one split per 256 keys; per (sequence, query head, split): D floats + max + sum
+    assert ea.attn_decode_workspace_size(64, 32, 8, 32768, 128) == 64 * 32 * 128 * 130 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 257, 64) == 2 * 66 * 4
+    assert ea.attn_decode_workspace_size(0, 1, 1, 1, 64) == 0
+
+
+def test_python_wrappers_reject_bad_tensors():
+    import torch
+
+    q = torch.zeros(1, 2, 4, 64)
+    with pytest.raises(ValueError):
+        ea.fwd(q, q, q)  # CPU tensors are refused before any library call
+    with pytest.raises(ValueError):
+        ea.fwd(q.half(), q.half(), q.half())
