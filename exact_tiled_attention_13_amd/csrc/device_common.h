@@ -31,6 +31,7 @@ namespace miattn {
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -43,6 +44,10 @@ constexpr float kLn2 = 0.69314718055994530942f;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Transposing 8-byte LDS read (see the layout note above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const __attribute__((address_space(3))) u16* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 __device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
@@ -66,6 +71,11 @@ __device__ __forceinline__ u16 f2bf(float x) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+// the same as one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }

@@ -4,64 +4,128 @@
 // Masks and KV caching; Transformers in Action section 9.4.1, Figure 9.8):
 // O = softmax(scale * Q K^T + mask) V, one query tile at a time, streaming
 // key/value tiles through on-chip memory with the online softmax: a running
-// row maximum m and denominator l, and the earlier partial output rescaled by
-// exp(m_old - m_new) whenever the maximum grows.  The score matrix never
-// leaves registers.
+// row maximum m and denominator l, and the partial output rescaled by
+// exp(m_old - m_new) when the maximum grows.  Scores never leave registers.
 //
-// gfx950 mapping.  One workgroup = NW wave64s = 32*NW query rows of one
-// (batch, query head).  Each wave owns 32 query rows and works in the
-// transposed frame, so that every lane owns exactly one query row:
+// gfx950 mapping.  A workgroup is NW wave64s; each wave owns QB blocks of 32
+// query rows of one (batch, query head) and works in the transposed frame,
+// where every lane owns one query row of each block:
 //
-//   S^T (keys x queries) = K * Q^T     v_mfma_f32_32x32x16_bf16, A = K from LDS,
-//                                      B = Q fragments held in registers
-//   O^T (d x queries)   += V^T * P^T   A = V^T via transposing LDS reads of the
-//                                      row-major V tile, B = P straight from
-//                                      the S^T accumulators (no shuffles)
+//   S^T (keys x queries) = K Q^T     v_mfma_f32_32x32x16_bf16; A = K from LDS,
+//                                    B = Q fragments held in registers
+//   O^T (d x queries)   += V^T P^T   A = V^T from transposing LDS reads of the
+//                                    row-major V tile; B = P taken straight
+//                                    from the S^T accumulators
 //
-// In both results lane l holds query row l%32, so the row maximum is a
-// per-lane max plus one exchange between the wave halves, the row sum stays
-// per lane until the epilogue, and the rescale by alpha needs no data
-// movement.  Softmax runs in base 2 with scale*log2(e) folded into one FMA.
-// K and V tiles of BN keys are staged through LDS (padded rows, no bank
-// conflicts for the 16-byte K reads and the transposing V reads); the next
-// tile's global loads are issued into registers before the current tile's
-// math, so HBM latency overlaps the MFMA work.
+// so the row maximum is a per-lane max plus one exchange between the wave
+// halves, the row sum stays per lane until the epilogue, and rescaling the
+// output needs no data movement.  Softmax runs in base 2 with
+// scale*log2(e) folded into one FMA; the row sum adds the fp32 P before
+// they are rounded to bf16 for the P V product (summing the rounded values
+// instead would move the log-sum-exp of rows with few keys by up to ~2e-3).
+//
+// Rescale threshold: the reference maximum m used in exp2(s - m) is only
+// moved when a row's true maximum exceeds it by more than 2^kThresh.  Any
+// reference value gives the same result (the final O = acc / l and
+// LSE = m + log2 l use the same m); the threshold only bounds P <= 2^8 and
+// lets the wave skip the rescale of its accumulators (a wave-uniform branch)
+// on almost every tile, so the accumulators stay in the matrix-core
+// registers.
+//
+// K and V tiles (BN keys) are copied HBM -> LDS by global_load_lds_dwordx4
+// (no staging registers) into an NS-stage ring: tiles j+1 .. j+NS-1 are in
+// flight while tile j is computed, and each wave waits (vmcnt) only for the
+// copies of the tile it is about to read.  Rows are stored unpadded, with
+// the 16-byte chunks of each row XOR-permuted (swz_k, swz_v below) so that
+// the 16-byte K reads and the transposing V reads are free of bank conflicts.
 #include "device_common.h"
 #include "launch.h"
+
+// Waves per workgroup and 32-row query blocks per wave.
+#ifndef FWD_NW
+#define FWD_NW 8
+#endif
+#ifndef FWD_QB
+#define FWD_QB 1
+#endif
 
 namespace miattn {
 namespace {
 
-template <int D, int NW>
+template <int D, int NW, int QB>
 struct FwdCfg {
-  static constexpr int BN = 64;               // keys per tile
-  static constexpr int BM = 32 * NW;          // query rows per workgroup
-  static constexpr int NT = 64 * NW;          // threads per workgroup
-  static constexpr int KST = D + 8;           // K row stride in LDS (bf16)
-  static constexpr int VST = D + 16;          // V row stride in LDS (bf16)
-  static constexpr int KS = D / 16;           // k-steps of Q K^T
-  static constexpr int DB = D / 32;           // 32-wide blocks of the head dim
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int LOADS = BN * CPR / NT; // 16-byte loads per thread per tensor per tile
-  static_assert(BN * CPR % NT == 0, "tile must split evenly over the workgroup");
+  static constexpr int BN = 64;                     // keys per tile
+  static constexpr int BM = 32 * QB * NW;           // query rows per workgroup
+  static constexpr int NT = 64 * NW;                // threads per workgroup
+  static constexpr int KS = D / 16;                 // k-steps of Q K^T
+  static constexpr int DB = D / 32;                 // 32-wide blocks of the head dim
+  static constexpr int TILE = BN * D;               // elements per K or V tile
+  static constexpr int LOADS = TILE * 2 / 1024;     // 1 KiB wave-loads per tensor per tile
+  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  static constexpr int NS = D == 64 ? 4 : 3;        // LDS stages (tiles in flight + 1)
+  static constexpr int VMEM_PER_TILE = 2 * LOADS_PER_WAVE;
+  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
 };
 
-template <int D, int NW, bool CAUSAL>
+constexpr float kThresh = 8.0f;
+
+// LDS chunk permutations.  gfx950 LDS has 64 banks of 4 bytes; a 16-byte
+// read is serviced 16 lanes at a time and a transposing 8-byte read 32 lanes
+// at a time, so every such lane group must touch distinct 16-byte slots
+// modulo 256 bytes.  The 16-byte chunks of tile row r are stored XOR-ed:
+//   K (read as 16 consecutive rows x one chunk):  D=128: r & 15;  D=64: (r >> 1) & 7
+//   V (read as 4 rows x 4 chunks per 32 lanes):   D=128: 4 (r & 3); D=64: 4 ((r >> 1) & 1)
+template <int D>
+__device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+template <int N>
+__device__ __forceinline__ void wait_vm_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+}
+// wait until this wave's copies of the current tile have landed, given that
+// `rem` later tiles (PER copies each) may still be in flight
+template <int PER, int R>
+__device__ __forceinline__ void wait_tile(int rem) {
+  if constexpr (R == 0) {
+    wait_vm_lds<0>();
+  } else {
+    if (rem >= R) wait_vm_lds<PER * R>();
+    else wait_tile<PER, R - 1>(rem);
+  }
+}
+
+typedef __attribute__((address_space(1))) const void gptr_t;
+typedef __attribute__((address_space(3))) void lptr_t;
+typedef __attribute__((address_space(3))) const u16 lds_u16;
+
+// Hide a per-lane LDS base from loop-invariant code motion (an empty asm
+// that emits nothing), so that each group of fragment reads is one add plus
+// reads whose constant row offsets fold into the DS immediate.
+__device__ __forceinline__ lds_u16* lds_base(lds_u16* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+template <int D, int NW, int QB, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
     int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq) {
-  using C = FwdCfg<D, NW>;
-  __shared__ __attribute__((aligned(16))) u16 Ks[C::BN * C::KST];
-  __shared__ __attribute__((aligned(16))) u16 Vs[C::BN * C::VST];
+  using C = FwdCfg<D, NW, QB>;
+  __shared__ __attribute__((aligned(1024))) u16 smem[C::NS][2][C::TILE];   // [stage][K, V][tile]
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, r32 = lane & 31;
+  const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // Workgroup -> (query tile, batch, head).  The query-tile index is the slow
   // one and runs from the last tile down, so under a causal mask the longest
-  // tiles start first; consecutive ids cover all (batch, head) pairs of one
-  // tile, and ids that share a (batch, head) are B*Hq apart.
+  // tiles start first; ids sharing a (batch, head) are B*Hq apart, which puts
+  // them on the same XCD (and L2) whenever B*Hq is a multiple of 8.
   const int BH = B * Hq;
   const int id = blockIdx.x;
   const int tq_slot = id / BH;
@@ -83,179 +147,236 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const u16* Vp = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
   u16* Op = O + ((size_t)b * Hq + hq) * (size_t)Tq * D;
 
-  // Keys this workgroup needs: [0, kend).
+  // keys this workgroup needs: [0, kend)
   int kend = 0;
   const int rows_end = min(q0 + C::BM, Lq);
   if (rows_end > q0) kend = CAUSAL ? min(Lk, rows_end + off) : Lk;
   if (kend < 0) kend = 0;
   const int ntiles = (kend + C::BN - 1) / C::BN;
 
-  // Per-wave extent: rows [wrow0, wrow0+32); last key any valid row of the
-  // wave may see (wave_kmax) and last key every row of the wave may see.
-  const int wrow0 = q0 + w * 32;
-  const int qrow = wrow0 + r32;
-  int wave_kmax = -1;
-  if (wrow0 < Lq) wave_kmax = CAUSAL ? min(Lk - 1, min(wrow0 + 31, Lq - 1) + off) : Lk - 1;
-  const int wave_kfull = CAUSAL ? min(Lk - 1, wrow0 + off) : Lk - 1;
+  // per query block: first row, last key any valid row may see, last key
+  // every row sees (beyond it the tile needs the mask)
+  const int wrow0 = q0 + w * 32 * QB;
+  int kmax[QB], kfull[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int r0 = wrow0 + 32 * qb;
+    kmax[qb] = -1;
+    if (r0 < Lq) kmax[qb] = CAUSAL ? min(Lk - 1, min(r0 + 31, Lq - 1) + off) : Lk - 1;
+    kfull[qb] = CAUSAL ? min(Lk - 1, r0 + off) : Lk - 1;
+  }
+  const int wave_kmax = kmax[QB - 1];  // the last block sees the most keys
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds row qrow, columns
-  // 16*ks + 8*h .. +7.
-  bf16x8 qf[C::KS];
-  {
-    const bool ok = qrow < Tq;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? qrow : 0) * D + 8 * h);
+  // Q fragments (B operand of S^T = K Q^T): row (wrow0 + 32 qb + r32),
+  // columns 16 ks + 8 h .. +7
+  bf16x8 qf[QB][C::KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = wrow0 + 32 * qb + r32;
+    const bool ok = row < Tq;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? row : 0) * D + 8 * h);
     const uint32_t flip = negq ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 x = ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
       x ^= flip;
-      qf[ks] = __builtin_bit_cast(bf16x8, x);
+      qf[qb][ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  f32x16 oacc[C::DB];
-#pragma unroll
-  for (int i = 0; i < C::DB; ++i) oacc[i] = f32x16{};
-  float m = kNegInf;   // running max of scale*log2(e)*s for this lane's row
-  float lsum = 0.f;    // running sum over this lane's half of the keys
-
-  u32x4 kreg[C::LOADS], vreg[C::LOADS];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = tid + i * C::NT;
-      const int row = idx / C::CPR, ch = idx % C::CPR;
-      const int key = kt * C::BN + row;
-      const bool ok = key < Lk;
-      const size_t g = (size_t)(ok ? key : 0) * D + ch * 8;
-      kreg[i] = ok ? *reinterpret_cast<const u32x4*>(Kp + g) : u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = ok ? *reinterpret_cast<const u32x4*>(Vp + g) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int idx = tid + i * C::NT;
-      const int row = idx / C::CPR, ch = idx % C::CPR;
-      *reinterpret_cast<u32x4*>(&Ks[row * C::KST + ch * 8]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&Vs[row * C::VST + ch * 8]) = vreg[i];
-    }
-  };
-
-  // transposing-read coordinates (see device_common.h)
-  const int tg = lane >> 4, tj = lane & 15;
-  const int tr_row = 4 * (tg >> 1) + (tj >> 2);        // + 32*kb + 16*sh (+8)
-  const int tr_col = 16 * (tg & 1) + 4 * (tj & 3);     // + 32*db
-
-  if (ntiles > 0) gload(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    __syncthreads();
-    sstore();
-    __syncthreads();
-    if (kt + 1 < ntiles) gload(kt + 1);
+  // HBM -> LDS copy of tile kt into stage st.  Each 1 KiB wave-load covers
+  // 1024/(2D) rows; lane l lands at byte 16 l of it, i.e. at (row, slot), and
+  // fetches the chunk that the swizzle stores in that slot.  Rows at or past
+  // Lk are replaced by row Lk-1 (finite data; those keys are masked).
+  auto issue = [&](int kt, int st) {
     const int kbase = kt * C::BN;
-    if (kbase > wave_kmax) continue;  // wave-uniform: tile fully masked for this wave
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u16* src = t ? Vp : Kp;
+#pragma unroll
+      for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+        const int li = w * C::LOADS_PER_WAVE + i;
+        const int e = li * 512 + lane * 8;
+        const int r = e / D, slot = (e % D) / 8;
+        const int ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
+        const int key = min(kbase + r, Lk - 1);
+        const u16* g = src + (size_t)key * D + ch * 8;
+        __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)&smem[st][t][li * 512], 16, 0, 0);
+      }
+    }
+  };
 
-    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks)
-    f32x16 s[2];
+  // per-lane LDS offsets (elements) of the fragments
+  //  K (A of S^T): row 32 kb + r32, logical chunk 2 ks + h
+  int koff[C::KS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const u16* kr = &Ks[(32 * kb + r32) * C::KST + 8 * h];
+  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = r32 * D + 8 * ((2 * ks + h) ^ swz_k<D>(r32));
+  //  V^T (A of O^T): transposing reads; 16-lane group g covers rows
+  //  vr..vr+3 (+16 sh + 32 kb, +8 for the upper half) and logical columns
+  //  32 db + 16 (g & 1) + 0..15
+  const int tg = lane >> 4, tj = lane & 15;
+  const int vr = 4 * (tg >> 1) + (tj >> 2);
+  const int vc0 = 2 * (tg & 1) + ((tj & 3) >> 1);
+  int voff[C::DB];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 16 * ks);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+  for (int db = 0; db < C::DB; ++db) voff[db] = vr * D + 8 * ((4 * db + vc0) ^ swz_v<D>(vr)) + 4 * (tj & 1);
+
+  f32x16 oacc[QB][C::DB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int i = 0; i < C::DB; ++i) oacc[qb][i] = f32x16{};
+  float m[QB], lsum[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = kNegInf;
+    lsum[qb] = 0.f;
+  }
+
+#pragma unroll
+  for (int p = 0; p < C::NS - 1; ++p)
+    if (p < ntiles) issue(p, p);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int st = kt % C::NS;
+    // this wave's copies of tile kt have landed and its LDS reads of tile
+    // kt-1 are done; after the barrier the same holds for every wave, so
+    // stage (kt-1) % NS can be refilled with tile kt+NS-1
+    wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - kt);
+    __builtin_amdgcn_s_barrier();
+    if (kt + C::NS - 1 < ntiles) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
+    const int kbase = kt * C::BN;
+    if (kbase > wave_kmax) continue;     // wave-uniform: tile fully masked for this wave
+
+    lds_u16* Ks = (lds_u16*)&smem[st][0][0];
+    lds_u16* Vs = (lds_u16*)&smem[st][1][0];
+
+    // ---- S^T = K Q^T
+    f32x16 s[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      // one per-lane base per k-step; the key-block offset folds into the
+      // instruction's immediate
+      lds_u16* kp = lds_base(Ks + koff[ks]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kp + 32 * kb * D);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
       }
     }
 
-    // ---- mask (only tiles that cross the padding or the diagonal)
-    const bool need_mask = kbase + C::BN - 1 > wave_kfull;
-    if (need_mask) {
-      const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
+    // ---- softmax per query block
+    bf16x8 pf[QB][2][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const bool need_mask = kbase + C::BN - 1 > kfull[qb];
+      const int qrow = wrow0 + 32 * qb + r32;
+      if (need_mask) {
+        const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            s[qb][kb][r] = key <= lim ? s[qb][kb][r] : kNegInf;
+          }
+      }
+      float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          s[kb][r] = key <= lim ? s[kb][r] : kNegInf;
-        }
-    }
-
-    // ---- online softmax update (base 2)
-    float mx = kNegInf;
+        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[qb][kb][r]), s[qb][kb][r + 1]);
+      mx = xhalf_max(mx);
+      const float mt = (mx == kNegInf) ? kNegInf : mx * c;
+      const bool grow = mt > m[qb] + kThresh;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mnew = fmaxf(m[qb], mt);
+        const float alpha = fast_exp2(m[qb] - ((mnew == kNegInf) ? 0.f : mnew));
+        m[qb] = mnew;
+        lsum[qb] *= alpha;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = xhalf_max(mx);
-    const float mt = (mx == kNegInf) ? kNegInf : mx * c;
-    const float mnew = fmaxf(m, mt);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
-    m = mnew;
-    const float nm = -muse;
-
-    bf16x8 pf[2][2];
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][r], c, nm));
-        if (need_mask) p = (s[kb][r] == kNegInf) ? 0.f : p;
-        ps += p;
-        pf[kb][r >> 3][r & 7] = static_cast<__bf16>(p);
+        for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      const float nm = (m[qb] == kNegInf) ? 0.f : -m[qb];
+      float ls = lsum[qb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh) {
-          const u16* vp = &Vs[(32 * kb + 16 * sh + tr_row) * C::VST + 32 * db + tr_col];
-          const u32x2 lo = lds_read_tr16(vp);
-          const u32x2 hi = lds_read_tr16(vp + 8 * C::VST);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][sh], oacc[db], 0, 0, 0);
+          // masked scores are -inf and c > 0, so exp2 gives exactly 0
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][8 * sh + e], c, nm));
+            const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][8 * sh + e + 1], c, nm));
+            ls += p0;
+            ls += p1;
+            pk[e >> 1] = pack2_bf16(p0, p1);
+          }
+          pf[qb][kb][sh] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
         }
+      lsum[qb] = ls;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      lds_u16* vrow = lds_base(Vs + voff[db]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          lds_u16* vp = vrow + (32 * kb + 16 * sh) * D;
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 8 * D);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][sh], oacc[qb][db], 0, 0, 0);
+        }
+    }
   }
 
-  // ---- epilogue: O = acc / l, LSE = ln(2) * (m + log2 l); empty rows -> 0, -inf
-  const float ltot = xhalf_sum(lsum);
-  const bool has = (qrow < Lq) && (ltot > 0.f);
-  const float inv = has ? 1.f / ltot : 0.f;
-  if (qrow < Tq) {
-    u16* orow = Op + (size_t)qrow * D;
+  // ---- epilogue: O = acc / l, LSE = ln(2) (m + log2 l); empty rows -> 0, -inf
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = wrow0 + 32 * qb + r32;
+    const float ltot = xhalf_sum(lsum[qb]);
+    const bool has = (qrow < Lq) && (ltot > 0.f);
+    const float inv = has ? 1.f / ltot : 0.f;
+    if (qrow < Tq) {
+      u16* orow = Op + (size_t)qrow * D;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * h;
-        u32x2 pk;
-        pk[0] = pack_bf16x2(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
-        pk[1] = pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d0) = pk;
-      }
-    if (LSE != nullptr && h == 0)
-      LSE[((size_t)b * Hq + hq) * Tq + qrow] = has ? (m + __log2f(ltot)) * kLn2 : kNegInf;
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * db + 8 * g4 + 4 * h;
+          u32x2 pk;
+          pk[0] = pack_bf16x2(oacc[qb][db][4 * g4 + 0] * inv, oacc[qb][db][4 * g4 + 1] * inv);
+          pk[1] = pack_bf16x2(oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d0) = pk;
+        }
+      if (LSE != nullptr && h == 0)
+        LSE[((size_t)b * Hq + hq) * Tq + qrow] = has ? (m[qb] + __log2f(ltot)) * kLn2 : kNegInf;
+    }
   }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int QB, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
-  using C = FwdCfg<D, NW>;
+  using C = FwdCfg<D, NW, QB>;
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const long long grid = (long long)nqt * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  const float c = fabsf(a.scale) * 1.4426950408889634f;
+  // c must be > 0 so that exp2(-inf * c) = 0 for masked keys.  For scale = 0
+  // the floor 1e-30 is exact in fp32: every |s| * 1e-30 rounds away against
+  // the row maximum, so all allowed keys get weight exactly 1.
+  const float c = fmaxf(fabsf(a.scale) * 1.4426950408889634f, 1e-30f);
   const int negq = a.scale < 0.f ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, a.kv_lens,
                      a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq);
   return hipGetLastError();
@@ -264,8 +385,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-  if (a.D == 64) return a.causal ? launch<64, 4, true>(a, st) : launch<64, 4, false>(a, st);
-  return a.causal ? launch<128, 4, true>(a, st) : launch<128, 4, false>(a, st);
+  if (a.D == 64) return a.causal ? launch<64, FWD_NW, FWD_QB, true>(a, st) : launch<64, FWD_NW, FWD_QB, false>(a, st);
+  return a.causal ? launch<128, FWD_NW, FWD_QB, true>(a, st) : launch<128, FWD_NW, FWD_QB, false>(a, st);
 }
 
 }  // namespace miattn
