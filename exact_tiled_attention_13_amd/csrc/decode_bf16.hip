@@ -8,19 +8,31 @@
 //
 // Split-K: the cache of one (sequence, KV head) is cut into splits of
 // kDecodeSplitKeys keys; each split is one wave that runs the online softmax
-// over its keys for all query heads of the group at once and writes an
-// un-normalised partial output with its running max and sum.  A second
-// kernel merges the splits of each (sequence, query head) with the same
-// rescale by exp(m_s - m) that the online softmax applies between tiles.
+// over its keys for all query heads of the group (up to 16 per wave) and
+// writes an un-normalised partial output with its running max and sum.  A
+// second kernel merges the splits of each (sequence, query head) with the
+// same rescale by exp(m_s - m) that the online softmax applies between tiles.
 //
 // Per 32-key tile a wave runs
-//   S^T (keys x heads) = K Q^T    v_mfma_f32_16x16x32_bf16, A = K rows loaded
-//                                 straight from HBM (16 B per lane), B = the
-//                                 group's queries (columns >= G are zero)
+//   S^T (keys x heads) = K Q^T    v_mfma_f32_16x16x32_bf16; A = K rows loaded
+//                                 from HBM into registers (16 B per lane),
+//                                 B = the group's queries (columns >= G zero)
 //   O^T (d x heads)   += V^T P^T  A = V^T by transposing reads of the V tile,
-//                                 which the wave stages in its own LDS slab.
-// The MFMA work is tiny next to the bytes moved; the matrix cores are used
-// because they need no bf16->fp32 unpacking and no cross-lane dot products.
+//                                 which is copied HBM -> LDS by
+//                                 global_load_lds_dwordx4 into the wave's own
+//                                 two-stage ring.
+// The next tile's K registers and V copies are issued before the current
+// tile's math, so every wave keeps ~32 KiB of loads in flight.  The V copies
+// (whole 1 KiB runs per instruction) are non-temporal: each cache byte is
+// read once, and on gfx950 nt reads stream faster.  The K fragment loads
+// touch each 128-byte line in two 64-byte halves from different
+// instructions, so they keep the default policy and let L2 serve the
+// second half.  The MFMA work
+// is tiny next to the bytes moved; the matrix cores are used because they
+// need no bf16 unpacking and no cross-lane dot products.
+#include <algorithm>
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -29,38 +41,111 @@ namespace {
 
 constexpr int kNW = 4;       // waves (= splits) per workgroup
 constexpr int kBN = 32;      // keys per tile
+// cache policy of the cache reads: non-temporal ("nt"), each byte is read once
+constexpr int kNonTemporal = 2;
 
+typedef __attribute__((address_space(1))) const void gptr_t;
+typedef __attribute__((address_space(3))) void lptr_t;
+typedef __attribute__((address_space(3))) const u16 lds_u16;
+
+// V tile chunk permutation: a transposing read (32 lanes) covers 8 rows x two
+// adjacent 16-byte chunks; the XOR spreads them over 16 distinct 16-byte
+// slots modulo 256 bytes (gfx950: 64 banks of 4 bytes).
+template <int D>
+__device__ __forceinline__ int swz_v(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+
+__device__ __forceinline__ lds_u16* lds_base(lds_u16* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// One unit of decode work: split s of sequence b for one block of up to 16
+// query heads of KV head hkv.  Keys [k0, k1).
+struct DecItem {
+  int b, hkv, hb, s, k0, k1, ntiles;
+};
+
+// Work items are enumerated sequence by sequence, split by split, head block
+// by head block: t = (prefix_splits(b) + s) * HBK + hbk.  Every wave computes
+// the prefix sums of the per-sequence split counts with a wave scan over 64
+// sequences at a time; lens0 caches this lane's length of the first 64.
+// Returns false once t is past the last item.  Results are wave-uniform.
+__device__ __forceinline__ bool find_item(int t, const int32_t* __restrict__ kv_lens, int lens0, int B, int S_max,
+                                          int HBK, int NHB, int lane, DecItem& it) {
+  const int u = t / HBK, hbk = t - u * HBK;
+  int base = 0;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int bb = c0 + lane;
+    const int L = c0 == 0 ? lens0 : (bb < B ? clampi(kv_lens[bb], 0, S_max) : 0);
+    const int ns = (L + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
+    int incl = ns;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int total = __shfl(incl, 63);
+    if (u < base + total) {
+      const unsigned long long hit = __ballot(base + incl > u);
+      const int first = __ffsll((long long)hit) - 1;
+      const int pre = base + __shfl(incl - ns, first);
+      const int Lb = __shfl(L, first);
+      it.b = __builtin_amdgcn_readfirstlane(c0 + first);
+      it.s = __builtin_amdgcn_readfirstlane(u - pre);
+      it.k0 = it.s * kDecodeSplitKeys;
+      it.k1 = __builtin_amdgcn_readfirstlane(min(it.k0 + kDecodeSplitKeys, Lb));
+      it.ntiles = (it.k1 - it.k0 + kBN - 1) / kBN;
+      it.hkv = hbk / NHB;
+      it.hb = hbk - it.hkv * NHB;
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// Persistent split kernel: the grid is sized to the chip (two workgroups per
+// CU) and wave W takes items W, W + #waves, ...; the next tile, including
+// the first tile of the wave's next item, is always in flight.
 template <int D>
 __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
     const u16* __restrict__ Qd, const u16* __restrict__ Kc, const u16* __restrict__ Vc,
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int Hq, int Hkv, int S_max, int NS, int NHB, float c, int negq) {
-  constexpr int VST = D + 16;          // LDS row stride (bf16) for conflict-free transposing reads
-  constexpr int KSTEPS = D / 32;       // k-steps of K Q^T
-  constexpr int DB = D / 16;           // 16-wide blocks of the head dim
-  constexpr int CPR = D / 8;           // 16-byte chunks per row
-  constexpr int VLOADS = kBN * CPR / 64;
-  __shared__ __attribute__((aligned(16))) u16 Vs[kNW][kBN * VST];
+    int B, int Hq, int Hkv, int S_max, int NS, int NHB, float c, int negq) {
+  constexpr int KSTEPS = D / 32;             // k-steps of K Q^T
+  constexpr int DB = D / 16;                 // 16-wide blocks of the head dim
+  constexpr int TILE = kBN * D;              // elements per V tile
+  constexpr int VLOADS = TILE * 2 / 1024;    // 1 KiB copies per V tile
+  constexpr int VM_PER_TILE = 2 * KSTEPS + VLOADS;   // vector-memory ops per tile per lane
+  __shared__ __attribute__((aligned(1024))) u16 Vs[kNW][2][TILE];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, j = lane & 15;
-  const int b = blockIdx.z;
-  const int hkv = blockIdx.y / NHB, hb = blockIdx.y - hkv * NHB;
-  const int split = blockIdx.x * kNW + w;
   const int G = Hq / Hkv;
+  const int HBK = Hkv * NHB;
+  const int NWAV = gridDim.x * kNW;
+  int t = blockIdx.x * kNW + w;
 
-  const int L = clampi(kv_lens[b], 0, S_max);
-  const int k0 = split * kDecodeSplitKeys;
-  const int k1 = min(k0 + kDecodeSplitKeys, L);
-  if (k0 >= k1) return;  // whole wave: no keys in this split (no barriers below)
+  const int lens0 = lane < B ? clampi(kv_lens[lane], 0, S_max) : 0;
+  DecItem cur;
+  if (!find_item(t, kv_lens, lens0, B, S_max, HBK, NHB, lane, cur)) return;
 
-  const int head = hb * 16 + j;        // this lane's query column within the group
-  const bool hv = head < G;
-  const int hq = hkv * G + (hv ? head : 0);
-
+  // per-item query fragments (B operand of S^T: column = head, d 32 ks + 8 g)
   bf16x8 qf[KSTEPS];
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qd + ((size_t)b * Hq + hq) * D + 8 * g);
+  int hq = 0;
+  bool hv = false;
+  auto load_q = [&](const DecItem& it) {
+    const int head = it.hb * 16 + j;
+    hv = head < G;
+    hq = it.hkv * G + (hv ? head : 0);
+    const u32x4* src = reinterpret_cast<const u32x4*>(Qd + ((size_t)it.b * Hq + hq) * D + 8 * g);
     const uint32_t flip = negq ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -68,61 +153,90 @@ __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
       x ^= flip;
       qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
-  }
+  };
+  load_q(cur);
 
-  const size_t slab = ((size_t)b * Hkv + hkv) * (size_t)S_max * D;
-  const u16* Kp = Kc + slab;
-  const u16* Vp = Vc + slab;
-  u16* vs = Vs[w];
+  // Issue tile `tile` of item `it`: K fragments into registers (A of S^T:
+  // key 16 kb + j, d 32 ks + 8 g .. +7) and the V rows into LDS stage BUF.
+  // Keys at or past k1 are replaced by key k1-1 (finite data; masked below).
+  u32x4 kf[2][2][KSTEPS];
+  auto issue = [&](auto BUF, const DecItem& it, int tile) {
+    constexpr int buf = decltype(BUF)::value;
+    const size_t slab = ((size_t)it.b * Hkv + it.hkv) * (size_t)S_max * D;
+    const u16* Kp = Kc + slab;
+    const u16* Vp = Vc + slab;
+    const int kt = it.k0 + tile * kBN;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = min(kt + 16 * kb + j, it.k1 - 1);
+      const u32x4* src = reinterpret_cast<const u32x4*>(Kp + (size_t)key * D + 8 * g);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) kf[buf][kb][ks] = src[4 * ks];
+    }
+#pragma unroll
+    for (int li = 0; li < VLOADS; ++li) {
+      const int e = li * 512 + lane * 8;
+      const int r = e / D, slot = (e % D) / 8;
+      const int ch = slot ^ swz_v<D>(r);
+      const int key = min(kt + r, it.k1 - 1);
+      __builtin_amdgcn_global_load_lds((gptr_t*)(Vp + (size_t)key * D + ch * 8),
+                                       (lptr_t*)&Vs[w][buf][li * 512], 16, 0, kNonTemporal);
+    }
+  };
+
+  // transposing-read offsets: group g covers rows 4 g + 0..3 (+16 for the
+  // upper half) and logical columns 16 db + 0..15
+  const int vr = 4 * g + (j >> 2);
+  int voff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    voff[db] = vr * D + 8 * ((2 * db + ((j & 3) >> 1)) ^ swz_v<D>(vr)) + 4 * (j & 1);
 
   f32x4 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
   float m = kNegInf, lsum = 0.f;
+  int tile = 0;
 
-  const int tr_row = 4 * g + (j >> 2);
-  const int tr_col = 4 * (j & 3);
-
-  for (int kt = k0; kt < k1; kt += kBN) {
-    // K fragments: A (16 keys x 32 d), lane holds key kt+16*kb+j, d 32*ks+8*g..+7
-    u32x4 kf[2][KSTEPS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = kt + 16 * kb + j;
-      const bool ok = key < k1;
-      const u32x4* src = reinterpret_cast<const u32x4*>(Kp + (size_t)(ok ? key : 0) * D + 8 * g);
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) kf[kb][ks] = ok ? src[4 * ks] : u32x4{0u, 0u, 0u, 0u};
+  // One step: tile `tile` of `cur` sits in buffer BUF.  The next (item,
+  // tile) is issued into the other buffer first (that buffer's LDS reads
+  // were consumed by the previous step's MFMAs), then the wave waits for the
+  // current tile only.  Returns false after the wave's last tile.
+  auto step = [&](auto BUF) -> bool {
+    constexpr int buf = decltype(BUF)::value;
+    DecItem nx = cur;
+    int ntile = tile + 1;
+    bool more = true;
+    if (ntile >= cur.ntiles) {
+      t += NWAV;
+      more = find_item(t, kv_lens, lens0, B, S_max, HBK, NHB, lane, nx);
+      ntile = 0;
     }
-    // V tile rows -> this wave's LDS slab; rows past the length are zero
-    u32x4 vr[VLOADS];
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int idx = lane + 64 * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      const int key = kt + row;
-      const bool ok = key < k1;
-      vr[i] = ok ? *reinterpret_cast<const u32x4*>(Vp + (size_t)(ok ? key : 0) * D + ch * 8)
-                 : u32x4{0u, 0u, 0u, 0u};
+    if (more) {
+      issue(std::integral_constant<int, buf ^ 1>{}, nx, ntile);
+      wait_vmcnt<VM_PER_TILE>();
+    } else {
+      wait_vmcnt<0>();
     }
 
+    const int kt = cur.k0 + tile * kBN;
     f32x4 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{};
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kb][ks]), qf[ks],
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[buf][kb][ks]), qf[ks],
                                                         s[kb], 0, 0, 0);
     }
-    const bool need_mask = kt + kBN > k1;
+    const bool need_mask = kt + kBN > cur.k1;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kt + 16 * kb + 4 * g + r;
-          s[kb][r] = key < k1 ? s[kb][r] : kNegInf;
+          s[kb][r] = key < cur.k1 ? s[kb][r] : kNegInf;
         }
     }
     float mx = kNegInf;
@@ -153,72 +267,113 @@ __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
 
-#pragma unroll
-    for (int i = 0; i < VLOADS; ++i) {
-      const int idx = lane + 64 * i;
-      const int row = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<u32x4*>(&vs[row * VST + ch * 8]) = vr[i];
-    }
-    // LDS operations of one wave complete in issue order; the fence keeps the
-    // compiler from moving the reads above the writes.
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // P^T element e of this lane is key 16*(e/4) + 4*g + e%4; the matching
-    // V^T fragment is rows 4*g.. and 16+4*g.. of column 16*db + j.
+    // P^T element e of this lane is key 16 (e/4) + 4 g + e%4; the matching
+    // V^T fragment is rows 4 g.. and 16 + 4 g.. of column 16 db + j.
+    lds_u16* vs = (lds_u16*)&Vs[w][buf][0];
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      const u16* vp = &vs[tr_row * VST + 16 * db + tr_col];
+      lds_u16* vp = lds_base(vs + voff[db]);
       const u32x2 lo = lds_read_tr16(vp);
-      const u32x2 hi = lds_read_tr16(vp + 16 * VST);
+      const u32x2 hi = lds_read_tr16(vp + 16 * D);
       const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[db], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  }
 
-  // sum over the four lane groups that share a query column
-  float lt = lsum + __shfl_xor(lsum, 16);
-  lt = xhalf_sum(lt);
-  if (hv) {
-    const size_t base = ((size_t)b * Hq + hq) * NS + split;
-    float* dst = ws_o + base * D;
+    if (tile == cur.ntiles - 1) {
+      // item done: write the partial (sum over the four lane groups that
+      // share a query column), reset, fetch the next item's queries
+      float lt = lsum + __shfl_xor(lsum, 16);
+      lt = xhalf_sum(lt);
+      if (hv) {
+        const size_t base = ((size_t)cur.b * Hq + hq) * NS + cur.s;
+        float* dst = ws_o + base * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = oacc[db];
-    if (g == 0) {
-      ws_ml[2 * base] = m;
-      ws_ml[2 * base + 1] = lt;
+        for (int db = 0; db < DB; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db + 4 * g) = oacc[db];
+        if (g == 0) {
+          ws_ml[2 * base] = m;
+          ws_ml[2 * base + 1] = lt;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
+      m = kNegInf;
+      lsum = 0.f;
+      if (more) load_q(nx);
     }
+    cur = nx;
+    tile = ntile;
+    return more;
+  };
+
+  issue(std::integral_constant<int, 0>{}, cur, 0);
+  while (step(std::integral_constant<int, 0>{}) && step(std::integral_constant<int, 1>{})) {
   }
 }
 
-// One wave per (query head, sequence): LSE-merge of the split partials.
+// One workgroup (4 waves) per (query head, sequence): LSE-merge of the split
+// partials.  Wave w takes splits w, w+4, ...; lane handles D/64 columns.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(
+__global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ O, float* __restrict__ LSE, int Hq, int S_max, int NS) {
   constexpr int PER = D / 64;
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+  __shared__ float red[4];
+  __shared__ float part[4][D + 1];
+  const int hq = blockIdx.x, b = blockIdx.y;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int L = clampi(kv_lens[b], 0, S_max);
   const int ns = (L + kDecodeSplitKeys - 1) / kDecodeSplitKeys;
   const size_t base = ((size_t)b * Hq + hq) * NS;
+
+  // global max of the split maxima
   float M = kNegInf;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ws_ml[2 * (base + s)]);
+  for (int s = threadIdx.x; s < ns; s += 256) M = fmaxf(M, ws_ml[2 * (base + s)]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float tot = 0.f;
-  for (int s = 0; s < ns; ++s) {
+#pragma unroll 4
+  for (int s = w; s < ns; s += 4) {
     const float wgt = fast_exp2(ws_ml[2 * (base + s)] - M);
     tot += wgt * ws_ml[2 * (base + s) + 1];
     const float* src = ws_o + (base + s) * D;
 #pragma unroll
     for (int i = 0; i < PER; ++i) acc[i] += wgt * src[lane + 64 * i];
   }
-  const bool has = tot > 0.f;
-  const float inv = has ? 1.f / tot : 0.f;
-  u16* dst = O + ((size_t)b * Hq + hq) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) dst[lane + 64 * i] = f2bf(acc[i] * inv);
-  if (LSE != nullptr && lane == 0) LSE[(size_t)b * Hq + hq] = has ? (M + __log2f(tot)) * kLn2 : kNegInf;
+  for (int i = 0; i < PER; ++i) part[w][lane + 64 * i] = acc[i];
+  if (lane == 0) part[w][D] = tot;
+  __syncthreads();
+  if (w == 0) {
+    const float T = part[0][D] + part[1][D] + part[2][D] + part[3][D];
+    const bool has = T > 0.f;
+    const float inv = has ? 1.f / T : 0.f;
+    u16* dst = O + ((size_t)b * Hq + hq) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int d = lane + 64 * i;
+      dst[d] = f2bf((part[0][d] + part[1][d] + part[2][d] + part[3][d]) * inv);
+    }
+    if (LSE != nullptr && lane == 0) LSE[(size_t)b * Hq + hq] = has ? (M + __log2f(T)) * kLn2 : kNegInf;
+  }
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;  // same value from every thread
+  }
+  return cached[dev];
 }
 
 template <int D>
@@ -228,13 +383,15 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const int NHB = (G + 15) / 16;
   const float c = fabsf(a.scale) * 1.4426950408889634f;
   const int negq = a.scale < 0.f ? 1 : 0;
-  const dim3 grid1((unsigned)((NS + kNW - 1) / kNW), (unsigned)(a.Hkv * NHB), (unsigned)a.B);
-  hipLaunchKernelGGL((decode_split_kernel<D>), grid1, dim3(64 * kNW), 0, st, (const u16*)a.q,
-                     (const u16*)a.k_cache, (const u16*)a.v_cache, a.kv_lens, a.ws_o, a.ws_ml, a.Hq, a.Hkv,
+  // two workgroups (8 waves) per CU, never more waves than work items
+  const long long items = (long long)a.B * NS * a.Hkv * NHB;
+  const long long wgs = std::min<long long>(2LL * cu_count(), (items + kNW - 1) / kNW);
+  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)wgs), dim3(64 * kNW), 0, st, (const u16*)a.q,
+                     (const u16*)a.k_cache, (const u16*)a.v_cache, a.kv_lens, a.ws_o, a.ws_ml, a.B, a.Hq, a.Hkv,
                      a.S_max, NS, NHB, c, negq);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(64), 0, st, a.ws_o,
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(256), 0, st, a.ws_o,
                      a.ws_ml, a.kv_lens, (u16*)a.o, a.lse, a.Hq, a.S_max, NS);
   return hipGetLastError();
 }

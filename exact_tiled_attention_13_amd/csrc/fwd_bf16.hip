@@ -41,12 +41,16 @@
 #include "device_common.h"
 #include "launch.h"
 
-// Waves per workgroup and 32-row query blocks per wave.
+// Waves per workgroup, 32-row query blocks per wave, and whether waves raise
+// their issue priority while they feed the matrix cores.
 #ifndef FWD_NW
 #define FWD_NW 8
 #endif
 #ifndef FWD_QB
 #define FWD_QB 1
+#endif
+#ifndef FWD_PRIO
+#define FWD_PRIO 0
 #endif
 
 namespace miattn {
@@ -61,10 +65,12 @@ struct FwdCfg {
   static constexpr int DB = D / 32;                 // 32-wide blocks of the head dim
   static constexpr int TILE = BN * D;               // elements per K or V tile
   static constexpr int LOADS = TILE * 2 / 1024;     // 1 KiB wave-loads per tensor per tile
-  static constexpr int LOADS_PER_WAVE = LOADS / NW;
+  // every wave issues the same number of copies (vmcnt accounting is per
+  // wave); when NW does not divide LOADS some waves repeat another wave's
+  // copy, which writes the same bytes to the same place
+  static constexpr int LOADS_PER_WAVE = (LOADS + NW - 1) / NW;
   static constexpr int NS = D == 64 ? 4 : 3;        // LDS stages (tiles in flight + 1)
   static constexpr int VMEM_PER_TILE = 2 * LOADS_PER_WAVE;
-  static_assert(LOADS % NW == 0, "tile loads must split evenly over the waves");
 };
 
 constexpr float kThresh = 8.0f;
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
       const u16* src = t ? Vp : Kp;
 #pragma unroll
       for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-        const int li = w * C::LOADS_PER_WAVE + i;
+        const int li = (w + NW * i) % C::LOADS;
         const int e = li * 512 + lane * 8;
         const int r = e / D, slot = (e % D) / 8;
         const int ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
@@ -251,6 +257,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     lds_u16* Vs = (lds_u16*)&smem[st][1][0];
 
     // ---- S^T = K Q^T
+    if (FWD_PRIO) __builtin_amdgcn_s_setprio(1);
     f32x16 s[QB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = f32x16{};
@@ -269,6 +276,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
 
     // ---- softmax per query block
+    if (FWD_PRIO) __builtin_amdgcn_s_setprio(0);
     bf16x8 pf[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -322,6 +330,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
 
     // ---- O^T += V^T P^T
+    if (FWD_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       lds_u16* vrow = lds_base(Vs + voff[db]);
@@ -340,6 +349,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
     }
   }
 
+  if (FWD_PRIO) __builtin_amdgcn_s_setprio(0);
   // ---- epilogue: O = acc / l, LSE = ln(2) (m + log2 l); empty rows -> 0, -inf
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {

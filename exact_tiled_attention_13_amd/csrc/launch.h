@@ -34,7 +34,7 @@ struct DecodeArgs {
 };
 
 // Keys handled by one decode split (one wave).
-constexpr int kDecodeSplitKeys = 256;
+constexpr int kDecodeSplitKeys = 512;
 
 inline int decode_num_splits(int S_max) { return (S_max + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
 inline size_t decode_ws_floats(int B, int Hq, int S_max, int D) {

@@ -87,10 +87,11 @@ def test_decode_validation(lib, args, code):
 
 
 def test_workspace_size(lib):
-    # one split per 256 keys; per (sequence, query head, split): D floats + max + sum
-    assert ea.attn_decode_workspace_size(64, 32, 8, 32768, 128) == 64 * 32 * 128 * 130 * 4
+    # one split per 512 keys; per (sequence, query head, split): D floats + max + sum
+    assert ea.attn_decode_workspace_size(64, 32, 8, 32768, 128) == 64 * 32 * 64 * 130 * 4
     assert ea.attn_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4
-    assert ea.attn_decode_workspace_size(1, 1, 1, 257, 64) == 2 * 66 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 512, 64) == 66 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 513, 64) == 2 * 66 * 4
     assert ea.attn_decode_workspace_size(0, 1, 1, 1, 64) == 0
 
 
