@@ -21,6 +21,9 @@ The float64 CPU oracle is timed on a bounded sample of the same workload
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -31,6 +34,16 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
+# kernel name (as rocprofv3 reports it, substring) -> sources it is built from
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h"],
+    "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
+    "decode_split_kernel": ["decode_bf16.hip", "device_common.h", "launch.h"],
+}
+COPY_BYTES = 1 << 30          # size of the calibration copy
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU * 2.4 GHz * 4096 dense bf16 flop/clk/CU
 PEAK_F32_MFMA_TFLOPS = 157.3
@@ -212,6 +225,81 @@ def cpu_baseline_decode(dec, budget_s):
                 sample=f"{nb} of {W.B} sequences of the decode workload (cache slabs upcast to float64), {dt:.1f} s")
 
 
+def sources_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        entry = json.load(fh).get(f"{kernel}/{workload}")
+    if not entry or entry.get("sources_sha256_16") != sources_hash(kernel):
+        return None
+    return entry["traffic_bytes_per_launch"]
+
+
+def copy_calibration(steps):
+    """A plain copy of COPY_BYTES, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x {steps}")
+
+
+def _pmc_rows(dirs, counter):
+    out = []
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter:
+                        out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def summarize_pmc(kernel, workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, command):
+    """Turn four rocprofv3 --pmc runs into a traffic entry of profiles/traffic.json."""
+    def mean_for(dirs, counter, sub):
+        v = [x for k, x in _pmc_rows(dirs, counter) if sub in k]
+        if not v:
+            raise SystemExit(f"no {counter} rows for {sub} under {dirs}")
+        return sum(v) / len(v), len(v)
+
+    copy_sub = "copy"
+    cf, _ = mean_for([copy_fetch_dir], "FETCH_SIZE", copy_sub)
+    cw, _ = mean_for([copy_write_dir], "WRITE_SIZE", copy_sub)
+    f_scale = (COPY_BYTES / 1024) / cf
+    w_scale = (COPY_BYTES / 1024) / cw
+    kf, nf = mean_for([fetch_dir], "FETCH_SIZE", kernel)
+    kw, nw = mean_for([write_dir], "WRITE_SIZE", kernel)
+    traffic = (kf * f_scale + kw * w_scale) * 1024
+    entry = dict(kernel=kernel, workload=workload, sources_sha256_16=sources_hash(kernel),
+                 fetch_kib_per_dispatch=kf, write_kib_per_dispatch=kw, dispatches=(nf, nw),
+                 copy_fetch_kib=cf, copy_write_kib=cw, copy_bytes=COPY_BYTES,
+                 fetch_scale=f_scale, write_scale=w_scale, traffic_bytes_per_launch=traffic, command=command)
+    path = os.path.join(PROFILES, "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            data = json.load(fh)
+    data[f"{kernel}/{workload}"] = entry
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps(entry, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,7 +309,20 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB copy (for scaling the FETCH_SIZE/WRITE_SIZE counters)")
+    ap.add_argument("--summarize-pmc", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                         "COPY_WRITE_DIR"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc output directories")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        k, fd, wd, cfd, cwd = args.summarize_pmc
+        summarize_pmc(k, args.workload, fd, wd, cfd, cwd, args.pmc_command)
+        return
+    if args.copy_calibration:
+        copy_calibration(max(1, args.steps))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -248,7 +349,8 @@ def main():
                     config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
                                 sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU"),
                     roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                  frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                                  frac=round(gbs / PEAK_HBM_GBS, 4),
+                                  traffic=traffic_for("decode_split_kernel", "decode"),
                                   kernels="decode_split + decode_merge"))
         if not args.no_cpu_baseline:
             line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
@@ -260,6 +362,7 @@ def main():
     check_graph_replay(torch, runner, pre["step"], pre["out"])
     ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
     W = pre["W"]
+    kname = "fwd_bf16_kernel" if W.dtype == "bf16" else "fwd_f32_kernel"
     tflops = pre["flops"] / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if W.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     line = dict(
@@ -270,8 +373,8 @@ def main():
         config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk, D=W.D, causal=W.causal,
                     flops_per_step=pre["flops"], parallelism="single GPU"),
         roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=peak, unit="TFLOP/s",
-                      frac=round(tflops / peak, 4), traffic=None, kernel="fwd_bf16_kernel" if W.dtype == "bf16"
-                      else "fwd_f32_kernel", kernel_ms=round(ms, 5)),
+                      frac=round(tflops / peak, 4), traffic=traffic_for(kname, args.workload), kernel=kname,
+                      kernel_ms=round(ms, 5)),
     )
     del pre, runner
     if args.workload == "causal" and not args.no_decode:
@@ -285,7 +388,8 @@ def main():
         line["decode"] = dict(workload=DW.note, value=round(gbs, 2), unit="GB/s", steps=dn, ms_per_step=round(dms, 5),
                               bytes_per_step=dec["bytes"], sum_lengths=int(np.sum(dec["w"]["lens"])),
                               roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                            frac=round(gbs / PEAK_HBM_GBS, 4), traffic=None,
+                                            frac=round(gbs / PEAK_HBM_GBS, 4),
+                                            traffic=traffic_for("decode_split_kernel", "decode"),
                                             kernels="decode_split + decode_merge"))
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget / 2)
