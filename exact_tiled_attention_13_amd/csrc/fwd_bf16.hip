@@ -7,9 +7,13 @@
 // row maximum m and denominator l, and the partial output rescaled by
 // exp(m_old - m_new) when the maximum grows.  Scores never leave registers.
 //
-// gfx950 mapping.  A workgroup is NW wave64s; each wave owns QB blocks of 32
-// query rows of one (batch, query head) and works in the transposed frame,
-// where every lane owns one query row of each block:
+// gfx950 mapping.  A workgroup owns BM = 32*NWG query rows of one (batch,
+// query head).  Its waves form KSPLIT key groups of NWG waves: every group
+// covers all BM rows (32 per wave) over its own contiguous share of the key
+// range, and the groups' partial (m, l, O) are merged through LDS at the end
+// with the same rescale rule.  KSPLIT > 1 shortens the chain of key tiles a
+// workgroup walks through, for grids too small to fill the chip.  Each wave
+// works in the transposed frame, where every lane owns one query row:
 //
 //   S^T (keys x queries) = K Q^T     v_mfma_f32_32x32x16_bf16; A = K from LDS,
 //                                    B = Q fragments held in registers
@@ -29,48 +33,58 @@
 // reference value gives the same result (the final O = acc / l and
 // LSE = m + log2 l use the same m); the threshold only bounds P <= 2^8 and
 // lets the wave skip the rescale of its accumulators (a wave-uniform branch)
-// on almost every tile, so the accumulators stay in the matrix-core
-// registers.
+// on almost every tile.
 //
 // K and V tiles (BN keys) are copied HBM -> LDS by global_load_lds_dwordx4
-// (no staging registers) into an NS-stage ring: tiles j+1 .. j+NS-1 are in
-// flight while tile j is computed, and each wave waits (vmcnt) only for the
-// copies of the tile it is about to read.  Rows are stored unpadded, with
-// the 16-byte chunks of each row XOR-permuted (swz_k, swz_v below) so that
-// the 16-byte K reads and the transposing V reads are free of bank conflicts.
+// (no staging registers) into an NS-stage ring per key group: tiles
+// j+1 .. j+NS-1 are in flight while tile j is computed, and each wave waits
+// (vmcnt) only for the copies of the tile it is about to read.  Rows are
+// stored unpadded, with the 16-byte chunks of each row XOR-permuted (swz_k,
+// swz_v below) so that the 16-byte K reads and the transposing V reads are
+// free of bank conflicts.
 #include "device_common.h"
 #include "launch.h"
 
-// Waves per workgroup, 32-row query blocks per wave, and whether waves raise
-// their issue priority while they feed the matrix cores.
-#ifndef FWD_NW
-#define FWD_NW 8
-#endif
-#ifndef FWD_QB
-#define FWD_QB 1
-#endif
-#ifndef FWD_PRIO
-#define FWD_PRIO 0
+// Workgroup count below which the launcher switches to 128-row workgroups
+// with two key groups (the chip has 256 CUs and holds two 256-row
+// workgroups per CU).
+#ifndef FWD_SPLIT_BELOW
+#define FWD_SPLIT_BELOW 512
 #endif
 
 namespace miattn {
 namespace {
 
-template <int D, int NW, int QB>
+template <int D, int NWG, int KSPLIT>
 struct FwdCfg {
-  static constexpr int BN = 64;                     // keys per tile
-  static constexpr int BM = 32 * QB * NW;           // query rows per workgroup
+  static constexpr int NW = NWG * KSPLIT;           // waves per workgroup
+  // keys per tile and LDS stages per key group (tiles in flight + 1).  One
+  // key group: 64-key tiles, 3-4 stages (64-96 KiB).  Two key groups: two
+  // stages each within 64 KiB in all, so that two workgroups share a CU.
+  static constexpr int BN = (KSPLIT > 1 && D == 128) ? 32 : 64;
+  static constexpr int NS = (KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3);
+  static constexpr int KB = BN / 32;                // 32-key blocks per tile
+  static constexpr int BM = 32 * NWG;               // query rows per workgroup
   static constexpr int NT = 64 * NW;                // threads per workgroup
   static constexpr int KS = D / 16;                 // k-steps of Q K^T
   static constexpr int DB = D / 32;                 // 32-wide blocks of the head dim
   static constexpr int TILE = BN * D;               // elements per K or V tile
   static constexpr int LOADS = TILE * 2 / 1024;     // 1 KiB wave-loads per tensor per tile
-  // every wave issues the same number of copies (vmcnt accounting is per
-  // wave); when NW does not divide LOADS some waves repeat another wave's
-  // copy, which writes the same bytes to the same place
-  static constexpr int LOADS_PER_WAVE = (LOADS + NW - 1) / NW;
-  static constexpr int NS = D == 64 ? 4 : 3;        // LDS stages (tiles in flight + 1)
+  // every wave of a group issues the same number of copies (vmcnt
+  // accounting is per wave); when NWG does not divide LOADS some waves
+  // repeat another wave's copy, which writes the same bytes to the same place
+  static constexpr int LOADS_PER_WAVE = (LOADS + NWG - 1) / NWG;
   static constexpr int VMEM_PER_TILE = 2 * LOADS_PER_WAVE;
+  static constexpr int RING = NS * 2 * TILE;        // u16 elements per key group
+  static constexpr int SMEM = KSPLIT * RING;
+  // merge through the (then idle) rings: the partial (m, l) of groups 1..,
+  // then their accumulators, DBR blocks of 32 columns per round
+  static constexpr int ML_FLOATS = (KSPLIT - 1) * NWG * 64 * 2;
+  static constexpr int BLK_FLOATS = (KSPLIT - 1) * NWG * 64 * 16;
+  static constexpr int AVAIL = SMEM / 2 - ML_FLOATS;
+  static constexpr int DBR = (DB * BLK_FLOATS <= AVAIL) ? DB : (DB % 2 == 0 && DB / 2 * BLK_FLOATS <= AVAIL) ? DB / 2 : 1;
+  static_assert(KSPLIT == 1 || BLK_FLOATS <= AVAIL, "merge buffer must fit in the rings");
+  static_assert(SMEM * 2 <= 160 * 1024, "LDS");
 };
 
 constexpr float kThresh = 8.0f;
@@ -116,17 +130,19 @@ __device__ __forceinline__ lds_u16* lds_base(lds_u16* p) {
   return p;
 }
 
-template <int D, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
+template <int D, int NWG, int KSPLIT, bool CAUSAL>
+__global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
     int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq) {
-  using C = FwdCfg<D, NW, QB>;
-  __shared__ __attribute__((aligned(1024))) u16 smem[C::NS][2][C::TILE];   // [stage][K, V][tile]
+  using C = FwdCfg<D, NWG, KSPLIT>;
+  __shared__ __attribute__((aligned(1024))) u16 smem[C::SMEM];   // [key group][stage][K, V][tile]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = w / NWG;          // key group
+  const int wg = w - kg * NWG;     // wave within the group = its 32-row block
 
   // Workgroup -> (query tile, batch, head).  The query-tile index is the slow
   // one and runs from the last tile down, so under a causal mask the longest
@@ -153,61 +169,60 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
   const u16* Vp = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
   u16* Op = O + ((size_t)b * Hq + hq) * (size_t)Tq * D;
 
-  // keys this workgroup needs: [0, kend)
+  // keys the workgroup needs: [0, kend) = ntiles_all tiles; key group g
+  // takes tiles [g * per, min((g + 1) * per, ntiles_all))
   int kend = 0;
   const int rows_end = min(q0 + C::BM, Lq);
   if (rows_end > q0) kend = CAUSAL ? min(Lk, rows_end + off) : Lk;
   if (kend < 0) kend = 0;
-  const int ntiles = (kend + C::BN - 1) / C::BN;
+  const int ntiles_all = (kend + C::BN - 1) / C::BN;
+  const int per = (ntiles_all + KSPLIT - 1) / KSPLIT;
+  const int t_begin = kg * per;
+  const int ntiles = max(0, min(per, ntiles_all - t_begin));
 
-  // per query block: first row, last key any valid row may see, last key
-  // every row sees (beyond it the tile needs the mask)
-  const int wrow0 = q0 + w * 32 * QB;
-  int kmax[QB], kfull[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int r0 = wrow0 + 32 * qb;
-    kmax[qb] = -1;
-    if (r0 < Lq) kmax[qb] = CAUSAL ? min(Lk - 1, min(r0 + 31, Lq - 1) + off) : Lk - 1;
-    kfull[qb] = CAUSAL ? min(Lk - 1, r0 + off) : Lk - 1;
-  }
-  const int wave_kmax = kmax[QB - 1];  // the last block sees the most keys
+  // this wave's rows [wrow0, wrow0 + 32): last key any valid row may see
+  // (kmax) and last key every row sees (kfull; past it a tile needs the mask)
+  const int wrow0 = q0 + 32 * wg;
+  const int qrow = wrow0 + r32;
+  int kmax = -1;
+  if (wrow0 < Lq) kmax = CAUSAL ? min(Lk - 1, min(wrow0 + 31, Lq - 1) + off) : Lk - 1;
+  const int kfull = CAUSAL ? min(Lk - 1, wrow0 + off) : Lk - 1;
 
-  // Q fragments (B operand of S^T = K Q^T): row (wrow0 + 32 qb + r32),
-  // columns 16 ks + 8 h .. +7
-  bf16x8 qf[QB][C::KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + 32 * qb + r32;
-    const bool ok = row < Tq;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? row : 0) * D + 8 * h);
+  // Q fragments (B operand of S^T = K Q^T): row qrow, columns 16 ks + 8 h .. +7
+  bf16x8 qf[C::KS];
+  {
+    const bool ok = qrow < Tq;
+    const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? qrow : 0) * D + 8 * h);
     const uint32_t flip = negq ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 x = ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
       x ^= flip;
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, x);
+      qf[ks] = __builtin_bit_cast(bf16x8, x);
     }
   }
 
-  // HBM -> LDS copy of tile kt into stage st.  Each 1 KiB wave-load covers
-  // 1024/(2D) rows; lane l lands at byte 16 l of it, i.e. at (row, slot), and
-  // fetches the chunk that the swizzle stores in that slot.  Rows at or past
-  // Lk are replaced by row Lk-1 (finite data; those keys are masked).
-  auto issue = [&](int kt, int st) {
-    const int kbase = kt * C::BN;
+  u16* ring = smem + kg * C::RING;
+
+  // HBM -> LDS copy of the group's tile lt (key tile t_begin + lt) into
+  // stage st.  Each 1 KiB wave-load covers 1024/(2D) rows; lane l lands at
+  // byte 16 l of it, i.e. at (row, slot), and fetches the chunk that the
+  // swizzle stores in that slot.  Rows at or past Lk are replaced by row
+  // Lk-1 (finite data; those keys are masked).
+  auto issue = [&](int lt, int st) {
+    const int kbase = (t_begin + lt) * C::BN;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const u16* src = t ? Vp : Kp;
 #pragma unroll
       for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-        const int li = (w + NW * i) % C::LOADS;
+        const int li = (wg + NWG * i) % C::LOADS;
         const int e = li * 512 + lane * 8;
         const int r = e / D, slot = (e % D) / 8;
         const int ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
         const int key = min(kbase + r, Lk - 1);
         const u16* g = src + (size_t)key * D + ch * 8;
-        __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)&smem[st][t][li * 512], 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)&ring[(st * 2 + t) * C::TILE + li * 512], 16, 0, 0);
       }
     }
   };
@@ -227,157 +242,210 @@ __global__ __launch_bounds__(64 * NW) void fwd_bf16_kernel(
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) voff[db] = vr * D + 8 * ((4 * db + vc0) ^ swz_v<D>(vr)) + 4 * (tj & 1);
 
-  f32x16 oacc[QB][C::DB];
+  f32x16 oacc[C::DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int i = 0; i < C::DB; ++i) oacc[qb][i] = f32x16{};
-  float m[QB], lsum[QB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = kNegInf;
-    lsum[qb] = 0.f;
-  }
+  for (int i = 0; i < C::DB; ++i) oacc[i] = f32x16{};
+  float m = kNegInf;   // reference maximum of scale*log2(e)*s for this lane's row
+  float lsum = 0.f;    // running sum over this lane's half of the keys
 
-#pragma unroll
-  for (int p = 0; p < C::NS - 1; ++p)
-    if (p < ntiles) issue(p, p);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt % C::NS;
-    // this wave's copies of tile kt have landed and its LDS reads of tile
-    // kt-1 are done; after the barrier the same holds for every wave, so
-    // stage (kt-1) % NS can be refilled with tile kt+NS-1
-    wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - kt);
-    __builtin_amdgcn_s_barrier();
-    if (kt + C::NS - 1 < ntiles) issue(kt + C::NS - 1, (kt + C::NS - 1) % C::NS);
-    const int kbase = kt * C::BN;
-    if (kbase > wave_kmax) continue;     // wave-uniform: tile fully masked for this wave
+  f32x16 s[C::KB];
+  bf16x8 pf[C::KB][2];
 
-    lds_u16* Ks = (lds_u16*)&smem[st][0][0];
-    lds_u16* Vs = (lds_u16*)&smem[st][1][0];
-
-    // ---- S^T = K Q^T
-    if (FWD_PRIO) __builtin_amdgcn_s_setprio(1);
-    f32x16 s[QB][2];
+  // ---- S^T = K Q^T for the tile in stage st
+  auto do_scores = [&](int st) {
+    lds_u16* Ks = (lds_u16*)&ring[(st * 2 + 0) * C::TILE];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) s[qb][0] = s[qb][1] = f32x16{};
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       // one per-lane base per k-step; the key-block offset folds into the
       // instruction's immediate
       lds_u16* kp = lds_base(Ks + koff[ks]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kp + 32 * kb * D);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][ks], s[qb][kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- softmax per query block
-    if (FWD_PRIO) __builtin_amdgcn_s_setprio(0);
-    bf16x8 pf[QB][2][2];
+  // ---- mask, online-softmax update and P for the tile starting at key kbase
+  auto do_softmax = [&](int kbase) {
+    const bool need_mask = kbase + C::BN - 1 > kfull;
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const bool need_mask = kbase + C::BN - 1 > kfull[qb];
-      const int qrow = wrow0 + 32 * qb + r32;
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            s[qb][kb][r] = key <= lim ? s[qb][kb][r] : kNegInf;
-          }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[qb][kb][r]), s[qb][kb][r + 1]);
-      mx = xhalf_max(mx);
-      const float mt = (mx == kNegInf) ? kNegInf : mx * c;
-      const bool grow = mt > m[qb] + kThresh;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float mnew = fmaxf(m[qb], mt);
-        const float alpha = fast_exp2(m[qb] - ((mnew == kNegInf) ? 0.f : mnew));
-        m[qb] = mnew;
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) oacc[qb][db] *= alpha;
-      }
-      const float nm = (m[qb] == kNegInf) ? 0.f : -m[qb];
-      float ls = lsum[qb];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          // masked scores are -inf and c > 0, so exp2 gives exactly 0
-          uint32_t pk[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(__builtin_fmaf(s[qb][kb][8 * sh + e], c, nm));
-            const float p1 = fast_exp2(__builtin_fmaf(s[qb][kb][8 * sh + e + 1], c, nm));
-            ls += p0;
-            ls += p1;
-            pk[e >> 1] = pack2_bf16(p0, p1);
-          }
-          pf[qb][kb][sh] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        for (int r = 0; r < 16; ++r) {
+          const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+          s[kb][r] = key <= lim ? s[kb][r] : kNegInf;
         }
-      lsum[qb] = ls;
     }
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+    mx = xhalf_max(mx);
+    const float mt = (mx == kNegInf) ? kNegInf : mx * c;
+    const bool grow = mt > m + kThresh;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - ((mnew == kNegInf) ? 0.f : mnew));
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+    }
+    const float nm = (m == kNegInf) ? 0.f : -m;
+    float ls = lsum;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        // masked scores are -inf and c > 0, so exp2 gives exactly 0
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * sh + e], c, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * sh + e + 1], c, nm));
+          ls += p0;
+          ls += p1;
+          pk[e >> 1] = pack2_bf16(p0, p1);
+        }
+        pf[kb][sh] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      }
+    lsum = ls;
+  };
 
-    // ---- O^T += V^T P^T
-    if (FWD_PRIO) __builtin_amdgcn_s_setprio(1);
+  // ---- O^T += V^T P^T with the V tile in stage st
+  auto do_pv = [&](int st) {
+    lds_u16* Vs = (lds_u16*)&ring[(st * 2 + 1) * C::TILE];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       lds_u16* vrow = lds_base(Vs + voff[db]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh) {
           lds_u16* vp = vrow + (32 * kb + 16 * sh) * D;
           const u32x2 lo = lds_read_tr16(vp);
           const u32x2 hi = lds_read_tr16(vp + 8 * D);
           const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[qb][kb][sh], oacc[qb][db], 0, 0, 0);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][sh], oacc[db], 0, 0, 0);
         }
     }
+  };
+
+  // ---- main loop.  Every key group runs `per` iterations, so that all
+  // waves meet the same barriers; a group with a shorter share idles
+  // through its last iteration.
+#pragma unroll
+  for (int p = 0; p < C::NS - 1; ++p)
+    if (p < ntiles) issue(p, p);
+  for (int lt = 0; lt < per; ++lt) {
+    const int st = lt % C::NS;
+    // this wave's copies of tile lt have landed and its LDS reads of tile
+    // lt-1 are done; after the barrier the same holds for every wave, so
+    // stage (lt-1) % NS can be refilled with tile lt+NS-1
+    if (lt < ntiles) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - lt);
+    __builtin_amdgcn_s_barrier();
+    if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
+    const int kbase = (t_begin + lt) * C::BN;
+    if (lt >= ntiles || kbase > kmax) continue;   // wave-uniform: nothing of this tile for the wave
+    do_scores(st);
+    do_softmax(kbase);
+    do_pv(st);
   }
 
-  if (FWD_PRIO) __builtin_amdgcn_s_setprio(0);
-  // ---- epilogue: O = acc / l, LSE = ln(2) (m + log2 l); empty rows -> 0, -inf
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = wrow0 + 32 * qb + r32;
-    const float ltot = xhalf_sum(lsum[qb]);
-    const bool has = (qrow < Lq) && (ltot > 0.f);
-    const float inv = has ? 1.f / ltot : 0.f;
-    if (qrow < Tq) {
-      u16* orow = Op + (size_t)qrow * D;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * db + 8 * g4 + 4 * h;
-          u32x2 pk;
-          pk[0] = pack_bf16x2(oacc[qb][db][4 * g4 + 0] * inv, oacc[qb][db][4 * g4 + 1] * inv);
-          pk[1] = pack_bf16x2(oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0) = pk;
-        }
-      if (LSE != nullptr && h == 0)
-        LSE[((size_t)b * Hq + hq) * Tq + qrow] = has ? (m[qb] + __log2f(ltot)) * kLn2 : kNegInf;
+  // ---- merge of the key groups' partials into group 0: with the combined
+  // reference M = max_g m_g, O = sum_g 2^(m_g - M) acc_g and l likewise.
+  // The rings are idle once every wave has passed the barrier below (each
+  // wave has waited for all of its copies and all of its LDS reads).
+  if constexpr (KSPLIT > 1) {
+    wait_vm_lds<0>();
+    __syncthreads();
+    float* part = reinterpret_cast<float*>(smem);
+    float* pblk = part + C::ML_FLOATS;
+    const int slot = (kg - 1) * NWG + wg;    // groups 1.. : this wave's slot
+    if (kg > 0) {
+      part[(2 * slot + 0) * 64 + lane] = m;
+      part[(2 * slot + 1) * 64 + lane] = lsum;
     }
+    float alpha[KSPLIT];
+#pragma unroll
+    for (int db0 = 0; db0 < C::DB; db0 += C::DBR) {
+      if (kg > 0) {
+#pragma unroll
+        for (int j = 0; j < C::DBR; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            pblk[((slot * C::DBR + j) * 16 + r) * 64 + lane] = oacc[db0 + j][r];
+      }
+      __syncthreads();
+      if (kg == 0) {
+        if (db0 == 0) {
+          // combined reference and the weight of every group's partial
+          float mg[KSPLIT];
+          mg[0] = m;
+          float mn = m;
+#pragma unroll
+          for (int g = 1; g < KSPLIT; ++g) {
+            mg[g] = part[(2 * ((g - 1) * NWG + wg) + 0) * 64 + lane];
+            mn = fmaxf(mn, mg[g]);
+          }
+          const float ref = (mn == kNegInf) ? 0.f : mn;
+          float ltot = 0.f;
+#pragma unroll
+          for (int g = 0; g < KSPLIT; ++g) {
+            alpha[g] = fast_exp2(mg[g] - ref);
+            const float lg = g == 0 ? lsum : part[(2 * ((g - 1) * NWG + wg) + 1) * 64 + lane];
+            ltot += lg * alpha[g];
+          }
+          m = mn;
+          lsum = ltot;
+        }
+#pragma unroll
+        for (int j = 0; j < C::DBR; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float acc = oacc[db0 + j][r] * alpha[0];
+#pragma unroll
+            for (int g = 1; g < KSPLIT; ++g)
+              acc += pblk[((((g - 1) * NWG + wg) * C::DBR + j) * 16 + r) * 64 + lane] * alpha[g];
+            oacc[db0 + j][r] = acc;
+          }
+      }
+      if (db0 + C::DBR < C::DB) __syncthreads();   // group 0 has read this round
+    }
+    if (kg > 0) return;
+  }
+
+  // ---- epilogue: O = acc / l, LSE = ln(2) (m + log2 l); empty rows -> 0, -inf
+  const float ltot = xhalf_sum(lsum);
+  const bool has = (qrow < Lq) && (ltot > 0.f);
+  const float inv = has ? 1.f / ltot : 0.f;
+  if (qrow < Tq) {
+    u16* orow = Op + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        u32x2 pk;
+        pk[0] = pack2_bf16(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
+        pk[1] = pack2_bf16(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + d0) = pk;
+      }
+    if (LSE != nullptr && h == 0)
+      LSE[((size_t)b * Hq + hq) * Tq + qrow] = has ? (m + __log2f(ltot)) * kLn2 : kNegInf;
   }
 }
 
-template <int D, int NW, int QB, bool CAUSAL>
+template <int D, int NWG, int KSPLIT, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
-  using C = FwdCfg<D, NW, QB>;
+  using C = FwdCfg<D, NWG, KSPLIT>;
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const long long grid = (long long)nqt * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -386,17 +454,28 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
   // the row maximum, so all allowed keys get weight exactly 1.
   const float c = fmaxf(fabsf(a.scale) * 1.4426950408889634f, 1e-30f);
   const int negq = a.scale < 0.f ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, QB, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, a.kv_lens,
                      a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq);
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
+  // 256-row workgroups with one key group fill the chip once there are two
+  // per CU; smaller problems take 128-row workgroups whose two key groups
+  // split the key range, which halves the longest chain of tiles and
+  // doubles the number of workgroups.
+  const long long wg256 = (long long)((a.Tq + 255) / 256) * a.B * a.Hq;
+  if (wg256 >= FWD_SPLIT_BELOW) return launch<D, 8, 1, CAUSAL>(a, st);
+  return launch<D, 4, 2, CAUSAL>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-  if (a.D == 64) return a.causal ? launch<64, FWD_NW, FWD_QB, true>(a, st) : launch<64, FWD_NW, FWD_QB, false>(a, st);
-  return a.causal ? launch<128, FWD_NW, FWD_QB, true>(a, st) : launch<128, FWD_NW, FWD_QB, false>(a, st);
+  if (a.D == 64) return a.causal ? launch_d<64, true>(a, st) : launch_d<64, false>(a, st);
+  return a.causal ? launch_d<128, true>(a, st) : launch_d<128, false>(a, st);
 }
 
 }  // namespace miattn

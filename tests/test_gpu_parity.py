@@ -177,6 +177,33 @@ def test_gqa_groups(G):
     run_case(2, 8, 8 // G, 200, 200, 128, torch.bfloat16, True, seed=10 + G)
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv", [(1, 8, 2), (2, 32, 8)])
+def test_both_workgroup_shapes(D, causal, B, Hq, Hkv):
+    """The launcher takes 256-row workgroups with one key group once there
+    are at least 512 of them (B=2, Hq=32, T=2048: 512) and 128-row
+    workgroups with two key groups below that (B=1, Hq=8: 64); both with
+    ragged lengths and GQA, rows sampled at the larger size."""
+    T = 2048
+    lens = [T, 1337, 700][:B] if B > 1 else [1999]
+    q = gen((B, Hq, T, D), 21, torch.bfloat16)
+    k = gen((B, Hkv, T, D), 22, torch.bfloat16)
+    v = gen((B, Hkv, T, D), 23, torch.bfloat16)
+    workloads.poison_tail_(k, lens)
+    workloads.poison_tail_(v, lens)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    sc = 1.0 / math.sqrt(D)
+    o, lse = ea.fwd(q, k, v, causal=causal, kv_lens=kv, scale=sc)
+    torch.cuda.synchronize()
+    rows = sample_rows(B, Hq, T, lens, 300, 9)
+    o_ref, l_ref = oracle.attention_rows(q.cpu(), k.cpu(), v.cpu(), rows, sc, causal, lens)
+    idx = tuple(torch.as_tensor(a, device="cuda") for a in np.array(rows).T)
+    check(o[idx], lse[idx], o_ref, l_ref, torch.bfloat16, f"B{B} Hq{Hq} Hkv{Hkv} T{T} D{D} causal={causal} lens={lens}")
+    for b, L in enumerate(lens):
+        assert torch.all(o[b, :, L:] == 0) and torch.all(torch.isneginf(lse[b, :, L:]))
+
+
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 2.0])
 def test_unusual_scales(scale):
     run_case(1, 2, 2, 100, 100, 64, torch.bfloat16, True, scale=scale, seed=7)
