@@ -30,7 +30,7 @@ SOURCES = ["api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode_bf16.hip"]
 FILE_FLAGS = {"fwd_bf16.hip": ["-fno-honor-nans"]}
 
 COMMON_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
     # keep packed-fp32 VALU instructions out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,

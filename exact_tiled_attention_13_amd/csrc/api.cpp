@@ -21,6 +21,22 @@ bool supported_d(int D) { return D == 64 || D == 128; }
 
 }  // namespace
 
+namespace miattn {
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;  // every thread stores the same value
+  }
+  return cached[dev];
+}
+
+}  // namespace miattn
+
 extern "C" {
 
 int attn_abi_version(void) { return 1; }

@@ -364,18 +364,6 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;  // same value from every thread
-  }
-  return cached[dev];
-}
-
 template <int D>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const int NS = decode_num_splits(a.S_max);
@@ -385,7 +373,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const int negq = a.scale < 0.f ? 1 : 0;
   // two workgroups (8 waves) per CU, never more waves than work items
   const long long items = (long long)a.B * NS * a.Hkv * NHB;
-  const long long wgs = std::min<long long>(2LL * cu_count(), (items + kNW - 1) / kNW);
+  const long long wgs = std::min<long long>(2LL * device_cu_count(), (items + kNW - 1) / kNW);
   hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)wgs), dim3(64 * kNW), 0, st, (const u16*)a.q,
                      (const u16*)a.k_cache, (const u16*)a.v_cache, a.kv_lens, a.ws_o, a.ws_ml, a.B, a.Hq, a.Hkv,
                      a.S_max, NS, NHB, c, negq);

@@ -43,12 +43,17 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Transposing 8-byte LDS read (see the layout note above).
-__device__ __forceinline__ u32x2 lds_read_tr16(const __attribute__((address_space(3))) u16* p) {
+// Transposing 8-byte LDS read (see the layout note above).  The pointer is
+// restrict-qualified so that the read carries alias-scope information: the
+// compiler's wait insertion then treats it like an ordinary LDS load instead
+// of waiting for every outstanding global->LDS copy before it (the kernels
+// order those copies against their reads with explicit vmcnt waits and
+// barriers).
+__device__ __forceinline__ u32x2 lds_read_tr16(const __attribute__((address_space(3))) u16* __restrict__ p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }
-__device__ __forceinline__ u32x2 lds_read_tr16(const u16* p) {
+__device__ __forceinline__ u32x2 lds_read_tr16(const u16* __restrict__ p) {
   s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }

@@ -51,6 +51,9 @@
 #ifndef FWD_SPLIT_BELOW
 #define FWD_SPLIT_BELOW 512
 #endif
+#ifndef FWD_ZIGZAG
+#define FWD_ZIGZAG 1
+#endif
 
 namespace miattn {
 namespace {
@@ -134,7 +137,7 @@ template <int D, int NWG, int KSPLIT, bool CAUSAL>
 __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
     u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
-    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq) {
+    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int zig) {
   using C = FwdCfg<D, NWG, KSPLIT>;
   __shared__ __attribute__((aligned(1024))) u16 smem[C::SMEM];   // [key group][stage][K, V][tile]
 
@@ -147,11 +150,15 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // Workgroup -> (query tile, batch, head).  The query-tile index is the slow
   // one and runs from the last tile down, so under a causal mask the longest
   // tiles start first; ids sharing a (batch, head) are B*Hq apart, which puts
-  // them on the same XCD (and L2) whenever B*Hq is a multiple of 8.
+  // them on the same XCD (and L2) whenever B*Hq is a multiple of 8.  When
+  // the whole grid is resident at once (zig), workgroups id and id + grid/2
+  // share a CU, so the second half of the ids runs from the first tile up:
+  // each CU then holds a long and a short causal tile, equal work in all.
   const int BH = B * Hq;
   const int id = blockIdx.x;
   const int tq_slot = id / BH;
-  const int qt = nqt - 1 - tq_slot;
+  const int half = (nqt + 1) / 2;
+  const int qt = (zig && tq_slot >= half) ? tq_slot - half : nqt - 1 - tq_slot;
   const int bh = id - tq_slot * BH;
   const int b = bh / Hq, hq = bh - b * Hq;
   const int hk = hq / (Hq / Hkv);
@@ -454,9 +461,13 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
   // the row maximum, so all allowed keys get weight exactly 1.
   const float c = fmaxf(fabsf(a.scale) * 1.4426950408889634f, 1e-30f);
   const int negq = a.scale < 0.f ? 1 : 0;
+  // at D=64 both shapes fit two workgroups per CU (64 KiB of LDS, at most
+  // 128 registers per lane), so a grid of at most two per CU is resident at
+  // once; at D=128 one per CU is, and heavy-first order is kept
+  const int zig = (CAUSAL && FWD_ZIGZAG && D == 64 && grid <= 2LL * device_cu_count()) ? 1 : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, st,
                      (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, a.kv_lens,
-                     a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq);
+                     a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig);
   return hipGetLastError();
 }
 

@@ -41,6 +41,9 @@ inline size_t decode_ws_floats(int B, int Hq, int S_max, int D) {
   return (size_t)B * Hq * decode_num_splits(S_max) * (size_t)(D + 2);
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cu_count();
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
