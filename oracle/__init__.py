@@ -15,14 +15,20 @@ Contents
 ``decode``           one new query per sequence against a contiguous KV cache.
 ``tiled_attention``  the tile-by-tile online-softmax algorithm (running max and
                      denominator, earlier partials rescaled), step by step.
+``attention_backward``  dQ, dK, dV of sum(dO * O) by the chain rule through the
+                     definition (softmax Jacobian row by row), float64.
+``backward_rows``    dQ of selected rows, for sampled checks at large sizes.
 
 Parity status: every function above is pinned by tests/test_oracle_pins.py
+and tests/test_oracle_backward_pins.py
 (closed forms, invariants, a textbook library routine and brute force on tiny
 inputs).  No page prints output values for the seeded workloads, so the
 seeded outputs themselves are pinned only through those properties.
 """
 
 from .attention import attention, attention_rows, decode, valid_lengths
+from .backward import attention_backward, backward_rows
 from .tiled import tiled_attention
 
-__all__ = ["attention", "attention_rows", "decode", "valid_lengths", "tiled_attention"]
+__all__ = ["attention", "attention_rows", "attention_backward", "backward_rows", "decode", "valid_lengths",
+           "tiled_attention"]

@@ -1,0 +1,124 @@
+"""Plain float64 gradients of attention.  TEST INFRASTRUCTURE ONLY.
+
+Only tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may use this module; the HIP product path never does.
+
+What is computed (sources, by page title and section):
+
+* The NumPy tiled-attention build guide, *Extending It*: the kernel extended
+  to produce dL/dQ, dL/dK and dL/dV by the chain rule through the softmax.
+* The self-attention interview question ("Self-Attention: Implementation,
+  Complexity ..."), Task 2 and Hint 2: the backward pass recomputes the
+  attention weights from the inputs instead of storing the N x N matrix;
+  only the forward's per-row statistics are kept.
+* The forward it differentiates is ``oracle.attention``: O = softmax(scale *
+  Q K^T + mask) V with causal (bottom-right), key-padding and grouped-query
+  semantics, rows with no allowed key giving O = 0.
+
+For one query head and its KV head, with P the softmax weights (zero on
+masked keys and on rows without keys) and dO the upstream gradient:
+
+    dV   = P^T dO                      (summed over the heads of a KV group)
+    dP   = dO V^T
+    Drow = sum_j P_ij dP_ij            (= sum_d dO_id O_id)
+    dS   = P * (dP - Drow)             (softmax Jacobian, row by row)
+    dQ   = scale * dS K
+    dK   = scale * dS^T Q              (summed over the heads of a KV group)
+
+These are the derivatives of the scalar L = sum(dO * O); every line is the
+chain rule through the definition above, evaluated in float64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _as_f64, valid_lengths
+
+
+def _weights(q_rows, k_all, scale, row_idx, lk, off, causal):
+    """Softmax weights P (n, lk) of a block of rows; zero where masked and
+    on rows without any allowed key."""
+    n = q_rows.shape[0]
+    if lk <= 0 or n == 0:
+        return np.zeros((n, max(lk, 0)), dtype=np.float64)
+    s = scale * (q_rows @ k_all[:lk].T)
+    j = np.arange(lk)[None, :]
+    allowed = np.ones((n, lk), dtype=bool)
+    if causal:
+        allowed &= j <= (row_idx[:, None] + off)
+    s = np.where(allowed, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    has = np.isfinite(m[:, 0])
+    m = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(allowed, np.exp(s - m), 0.0)
+    l = e.sum(axis=1, keepdims=True)
+    p = np.where(has[:, None], e / np.where(l > 0, l, 1.0), 0.0)
+    return p
+
+
+def attention_backward(q, k, v, do, scale, causal=False, kv_lens=None, row_chunk=256):
+    """dQ, dK, dV (float64 numpy arrays) of L = sum(dO * attention(q, k, v)).
+
+    q, do: (B, Hq, Tq, D); k, v: (B, Hkv, Tk, D).  Padding query rows (and
+    rows without keys) have zero weights, so they contribute nothing and get
+    dQ = 0; keys past a sequence's length get dK = dV = 0.
+    """
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    if Hq % Hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    lk_all, lq_all = valid_lengths(B, Tq, Tk, kv_lens)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        lk, lq = lk_all[b], lq_all[b]
+        off = lk - lq
+        if lk <= 0:
+            continue
+        for h in range(Hq):
+            hk = h // G
+            kk, vv = k[b, hk, :lk], v[b, hk, :lk]
+            for r0 in range(0, lq, row_chunk):
+                rows = np.arange(r0, min(lq, r0 + row_chunk))
+                p = _weights(q[b, h, rows], kk, scale, rows, lk, off, causal)   # (n, lk)
+                g = do[b, h, rows]                                              # (n, D)
+                dv[b, hk, :lk] += p.T @ g
+                dp = g @ vv.T
+                drow = (p * dp).sum(axis=1, keepdims=True)
+                ds = p * (dp - drow)
+                dq[b, h, rows] = scale * (ds @ kk)
+                dk[b, hk, :lk] += scale * (ds.T @ q[b, h, rows])
+    return dq, dk, dv
+
+
+def backward_rows(q, k, v, do, rows, scale, causal=False, kv_lens=None):
+    """dQ of selected (b, h, i) rows only (float64, shape (len(rows), D)).
+
+    A row's dQ needs only that row's softmax, so this reaches sizes where the
+    full backward is too slow on the CPU."""
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    lk_all, lq_all = valid_lengths(B, Tq, Tk, kv_lens)
+    out = np.zeros((len(rows), D), dtype=np.float64)
+    for n, (b, h, i) in enumerate(rows):
+        lk, lq = lk_all[b], lq_all[b]
+        if i >= lq or lk <= 0:
+            continue
+        hk = h // G
+        kk = _as_f64(k[b, hk, :lk])
+        vv = _as_f64(v[b, hk, :lk])
+        qi = _as_f64(q[b, h, i:i + 1])
+        g = _as_f64(do[b, h, i:i + 1])
+        p = _weights(qi, kk, scale, np.array([i]), lk, lk - lq, causal)
+        dp = g @ vv.T
+        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+        out[n] = scale * (ds @ kk)[0]
+    return out
