@@ -6,9 +6,11 @@ device memory and the current stream only.
 
     o, lse = fwd(q, k, v, causal=True)                 # prefill
     o, lse = decode(q, k_cache, v_cache, kv_lens)      # one KV-cache decode step
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True) # gradients of the prefill
 
 The C-ABI functions are re-exported under their C names (``attn_fwd``,
-``attn_decode``, ``attn_decode_workspace_size``, ``attn_strerror``).
+``attn_decode``, ``attn_decode_workspace_size``, ``attn_bwd``,
+``attn_bwd_workspace_size``, ``attn_strerror``).
 """
 
 from __future__ import annotations
@@ -22,6 +24,8 @@ from ._lib import (  # noqa: F401
     MIATTN_F32,
     MiattnError,
     attn_abi_version,
+    attn_bwd,
+    attn_bwd_workspace_size,
     attn_decode,
     attn_decode_workspace_size,
     attn_fwd,
@@ -29,8 +33,8 @@ from ._lib import (  # noqa: F401
     load,
 )
 
-__all__ = ["fwd", "decode", "attn_fwd", "attn_decode", "attn_decode_workspace_size", "attn_strerror",
-           "MiattnError", "load"]
+__all__ = ["fwd", "decode", "bwd", "attn_fwd", "attn_decode", "attn_decode_workspace_size", "attn_bwd",
+           "attn_bwd_workspace_size", "attn_strerror", "MiattnError", "load"]
 
 
 def _torch():
@@ -130,3 +134,43 @@ def decode(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, workspac
     attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv,
                 S_max, D, scale, lens.data_ptr(), ws_ptr, ws_bytes, dt, stream)
     return o, l_out
+
+
+def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_lens=None, scale: float | None = None, workspace=None,
+        dq=None, dk=None, dv=None):
+    """Gradients of the prefill.  q, o, do (B,Hq,Tq,D) and k, v (B,Hkv,Tk,D) bf16, lse (B,Hq,Tq) float32,
+    all on the GPU; o and lse as fwd returned them with the same causal / kv_lens / scale.
+
+    Returns (dq, dk, dv) in bf16 with the shapes of q, k, v.
+    """
+    torch = _torch()
+    if q.dtype != torch.bfloat16:
+        raise ValueError("bwd takes bfloat16 tensors")
+    B, Hq, Tq, D = q.shape
+    for name, t in (("q", q), ("o", o), ("do", do)):
+        _check_tensor(name, t, 4, torch.bfloat16, q.device)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} does not match q {tuple(q.shape)}")
+    _check_tensor("k", k, 4, torch.bfloat16, q.device)
+    _check_tensor("v", v, 4, torch.bfloat16, q.device)
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    _check_tensor("lse", lse, 3, torch.float32, q.device)
+    if lse.shape != (B, Hq, Tq):
+        raise ValueError("lse must be (B, Hq, Tq)")
+    Hkv, Tk = k.shape[1], k.shape[2]
+    lens = _lens(kv_lens, B, q.device, False)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = attn_bwd_workspace_size(B, Hq, Tq)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+             dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Tq, Tk, D, scale, 1 if causal else 0,
+             0 if lens is None else lens.data_ptr(), workspace.data_ptr(),
+             workspace.numel() * workspace.element_size(), MIATTN_BF16, stream)
+    return dq, dk, dv

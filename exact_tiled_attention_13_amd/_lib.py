@@ -13,7 +13,8 @@ LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_PKG, "libmiattn.so")
 MIATTN_F32 = 0
 MIATTN_BF16 = 1
 
-EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_strerror", "attn_abi_version")
+EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_bwd_workspace_size", "attn_bwd",
+            "attn_strerror", "attn_abi_version")
 
 _lib = None
 
@@ -43,6 +44,10 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, i, vp]
     lib.attn_decode.restype = i
+    lib.attn_bwd_workspace_size.argtypes = [i, i, i]
+    lib.attn_bwd_workspace_size.restype = sz
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, sz, i, vp]
+    lib.attn_bwd.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -61,6 +66,10 @@ def attn_abi_version() -> int:
 
 def attn_decode_workspace_size(B: int, Hq: int, Hkv: int, S_max: int, D: int) -> int:
     return int(load().attn_decode_workspace_size(B, Hq, Hkv, S_max, D))
+
+
+def attn_bwd_workspace_size(B: int, Hq: int, Tq: int) -> int:
+    return int(load().attn_bwd_workspace_size(B, Hq, Tq))
 
 
 def _check(code: int) -> int:
@@ -82,4 +91,13 @@ def attn_decode(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, D, scale, kv_len
     code = load().attn_decode(q or None, k_cache or None, v_cache or None, o or None, lse or None, B, Hq, Hkv,
                               S_max, D, float(scale), kv_lens or None, workspace or None, workspace_bytes, dtype,
                               stream or None)
+    return _check(code) if check else code
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, D, scale, causal, kv_lens, workspace,
+             workspace_bytes, dtype, stream, check=True):
+    """Raw C-ABI call; pointers are integers (0 = NULL)."""
+    code = load().attn_bwd(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
+                           dk or None, dv or None, B, Hq, Hkv, Tq, Tk, D, float(scale), int(causal),
+                           kv_lens or None, workspace or None, workspace_bytes, dtype, stream or None)
     return _check(code) if check else code

@@ -39,7 +39,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 1; }
+int attn_abi_version(void) { return 2; }
 
 const char* attn_strerror(int code) {
   switch (code) {
@@ -47,7 +47,7 @@ const char* attn_strerror(int code) {
     case MIATTN_ERR_NULL: return "a required pointer is NULL";
     case MIATTN_ERR_SHAPE: return "bad shape or scale (sizes must be > 0, Hq % Hkv == 0, scale finite)";
     case MIATTN_ERR_UNSUPPORTED: return "unsupported argument (D must be 64 or 128, dtype 0/1, causal 0/1)";
-    case MIATTN_ERR_WORKSPACE: return "decode workspace missing or smaller than attn_decode_workspace_size()";
+    case MIATTN_ERR_WORKSPACE: return "workspace missing or smaller than the size the matching *_workspace_size() gives";
     case MIATTN_ERR_HIP: return g_hip_msg;
     default: return "unknown error code";
   }
@@ -96,6 +96,30 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
   const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
   miattn::DecodeArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D};
   hipError_t e = miattn::launch_decode_bf16(a, st);
+  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+}
+
+size_t attn_bwd_workspace_size(int B, int Hq, int Tq) {
+  if (B <= 0 || Hq <= 0 || Tq <= 0) return 0;
+  return miattn::bwd_ws_floats(B, Hq, Tq) * sizeof(float);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+             const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
+    return MIATTN_ERR_SHAPE;
+  if (!supported_d(D) || dtype != MIATTN_BF16 || (causal != 0 && causal != 1)) return MIATTN_ERR_UNSUPPORTED;
+  // 128 query rows (dQ) and 128 keys (dK, dV) per workgroup, 32 rows per prep block
+  if ((long long)((Tq + 127) / 128) * B * Hq > 0x7fffffffLL || (long long)((Tk + 127) / 128) * B * Hkv > 0x7fffffffLL ||
+      ((long long)B * Hq * Tq + 31) / 32 > 0x7fffffffLL)
+    return MIATTN_ERR_SHAPE;
+  const size_t need = attn_bwd_workspace_size(B, Hq, Tq);
+  if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+  miattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, kv_lens, B, Hq, Hkv, Tq, Tk, D, scale, causal,
+                    static_cast<float*>(workspace)};
+  hipError_t e = miattn::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : hip_fail(e);
 }
 

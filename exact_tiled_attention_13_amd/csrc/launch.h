@@ -33,6 +33,25 @@ struct DecodeArgs {
   float* ws_ml;            // split partial (max, sum)
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* kv_lens;  // device int32[B] or null
+  int B, Hq, Hkv, Tq, Tk, D;
+  float scale;
+  int causal;
+  float* ws;               // 2 * B * Hq * Tq floats: per-row dO.O, then LSE * log2(e)
+};
+
+inline size_t bwd_ws_floats(int B, int Hq, int Tq) { return 2 * (size_t)B * Hq * Tq; }
+
 // Keys handled by one decode split (one wave).
 constexpr int kDecodeSplitKeys = 512;
 
@@ -47,5 +66,6 @@ int device_cu_count();
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 
 }  // namespace miattn

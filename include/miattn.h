@@ -70,7 +70,7 @@ enum {
   MIATTN_ERR_NULL = -1,        /* a required pointer is NULL */
   MIATTN_ERR_SHAPE = -2,       /* size <= 0, Hq % Hkv != 0, non-finite scale, or grid too large */
   MIATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, causal not 0/1 */
-  MIATTN_ERR_WORKSPACE = -4,   /* decode workspace missing or too small */
+  MIATTN_ERR_WORKSPACE = -4,   /* workspace missing or too small */
   MIATTN_ERR_HIP = -5          /* the HIP runtime refused a launch; see attn_strerror */
 };
 
@@ -101,6 +101,34 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 int B, int Hq, int Hkv, int S_max, int D, float scale,
                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
                 int dtype, void* stream);
+
+/* Bytes of device workspace attn_bwd needs: 8 * B * Hq * Tq. */
+size_t attn_bwd_workspace_size(int B, int Hq, int Tq);
+
+/*
+ * Gradients of the prefill attention (bf16 only; dtype must be MIATTN_BF16,
+ * MIATTN_F32 gives MIATTN_ERR_UNSUPPORTED).  Sources: the NumPy
+ * tiled-attention build guide, section Extending It (dQ, dK, dV by the chain
+ * rule through the softmax), and the self-attention interview question,
+ * Task 2 and Hint 2 (the backward recomputes the attention weights tile by
+ * tile from Q, K and the saved per-row statistics instead of storing them).
+ *
+ * Given the forward's inputs q, k, v, its output o and lse (as attn_fwd
+ * wrote them, same scale, causal and kv_lens), and dout = dL/dO [B, Hq, Tq,
+ * D], writes dq [B, Hq, Tq, D], dk and dv [B, Hkv, Tk, D] (bf16, same
+ * layouts as q, k, v):
+ *   P = exp(scale * Q K^T + mask - lse),  dV = P^T dO,  dP = dO V^T,
+ *   dS = P * (dP - rowsum(dO * O)),  dQ = scale dS K,  dK = scale dS^T Q,
+ * with dK and dV of a KV head summed over the query heads sharing it.  Rows
+ * with lse = -inf or that are padding get no gradient (dq = 0); keys at or
+ * past Lk get dk = dv = 0.  workspace: device memory of at least
+ * attn_bwd_workspace_size(B, Hq, Tq) bytes (per-row scratch; contents on
+ * entry do not matter); dq, dk, dv must not alias any input.  Every output
+ * element is written.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
+             const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /* Static text for a return code; for MIATTN_ERR_HIP, the last HIP error seen
  * by the calling thread. */

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert ea.attn_abi_version() == 1
+    assert ea.attn_abi_version() == 2
 
 
 def test_strerror_covers_codes(lib):
@@ -93,6 +93,25 @@ def test_workspace_size(lib):
     assert ea.attn_decode_workspace_size(1, 1, 1, 512, 64) == 66 * 4
     assert ea.attn_decode_workspace_size(1, 1, 1, 513, 64) == 2 * 66 * 4
     assert ea.attn_decode_workspace_size(0, 1, 1, 1, 64) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1), (dict(lse=0), -1), (dict(dout=0), -1), (dict(dq=0), -1), (dict(dv=0), -1), (dict(o=0), -1),
+    (dict(B=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(scale=float("nan")), -2), (dict(Tk=0), -2),
+    (dict(D=96), -3), (dict(dtype=0), -3), (dict(causal=3), -3),
+    (dict(workspace=0), -4), (dict(workspace_bytes=10), -4),
+])
+def test_bwd_validation(lib, args, code):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, Hq=2, Hkv=1,
+             Tq=8, Tk=8, D=64, scale=0.125, causal=0, kv_lens=0, workspace=FAKE, workspace_bytes=1 << 40,
+             dtype=1, stream=0)
+    a.update(args)
+    assert ea.attn_bwd(**a, check=False) == code
+
+
+def test_bwd_workspace_size(lib):
+    assert ea.attn_bwd_workspace_size(4, 16, 1024) == 8 * 4 * 16 * 1024
+    assert ea.attn_bwd_workspace_size(0, 16, 1024) == 0
 
 
 def test_python_wrappers_reject_bad_tensors():
