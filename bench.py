@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal|long|ragged|decode|single]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal|long|ragged|decode|single] [--backward]
 
 A step is one pass of the hot path over one batch of synthetic, seeded input
 already resident in HBM.  The headline line measures the causal prefill
@@ -9,7 +9,9 @@ workload (B=4, H=16, T=1024, D=64, bf16) in TFLOP/s of algorithmic work
 (4*D flops per unmasked (query, key) pair); the same run also times one
 KV-cache decode step of the GQA decode workload (B=64, Hq=32, Hkv=8, D=128,
 lengths 1024..32768) in GB/s of algorithmic bytes (the K/V rows each sequence
-needs plus q, o, lse and lengths), reported under "decode".  Steps are
+needs plus q, o, lse and lengths), reported under "decode", and the gradients
+of the causal workload (10*D flops per unmasked pair: the five products of
+the backward), reported under "backward".  Steps are
 replayed from a HIP graph (a fixed number of calls per graph) so that host
 launch overhead does not enter the timing; the kernels are timed with HIP
 events recorded on the stream they run on.
@@ -141,6 +143,64 @@ def setup_prefill(torch, name):
     io_bytes = (2 * q.numel() + k.numel() + v.numel()) * elem + lse.numel() * 4
     keep = (q, k, v, kv, o, lse)
     return dict(w=w, W=W, step=step, flops=flops, io_bytes=io_bytes, keep=keep, out=(o, lse))
+
+
+def setup_backward(torch, name):
+    """Gradients of a prefill workload: q, k, v of the workload, a seeded dO,
+    and O, LSE from one forward call."""
+    import exact_tiled_attention_13_amd as ea
+    from exact_tiled_attention_13_amd import workloads
+
+    w = workloads.make(name, device="cpu")
+    W = w["workload"]
+    if W.dtype != "bf16":
+        raise SystemExit("the backward pass is bf16 only")
+    q, k, v = (w[x].cuda() for x in ("q", "k", "v"))
+    g = torch.Generator().manual_seed(1)
+    do = workloads.randn_bf16(tuple(q.shape), g).cuda()
+    kv = None if w["kv_lens"] is None else w["kv_lens"].cuda()
+    o, lse = ea.fwd(q, k, v, causal=W.causal, kv_lens=kv, scale=W.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = ea.attn_bwd_workspace_size(W.B, W.Hq, W.Tq)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+            dk.data_ptr(), dv.data_ptr(), W.B, W.Hq, W.Hkv, W.Tq, W.Tk, W.D, W.scale, int(W.causal),
+            0 if kv is None else kv.data_ptr(), ws.data_ptr(), nbytes, ea.MIATTN_BF16)
+
+    def step():
+        ea.attn_bwd(*args, torch.cuda.current_stream().cuda_stream)
+
+    pairs = prefill_pairs(W.B, W.Hq, W.Tq, W.Tk, W.causal, w["lens"])
+    return dict(w=w, W=W, step=step, flops=10 * W.D * pairs, keep=(q, k, v, do, kv, o, lse, ws),
+                out=(dq, dk, dv))
+
+
+def cpu_baseline_backward(name, budget_s):
+    import oracle
+    from exact_tiled_attention_13_amd import workloads
+
+    w = workloads.make(name, device="cpu")
+    W = w["workload"]
+    q, k, v = w["q"], w["k"], w["v"]
+    do = workloads.randn_bf16(tuple(q.shape), __import__("torch").Generator().manual_seed(1))
+    G = W.Hq // W.Hkv
+    done, heads = 0, 0
+    t0 = time.perf_counter()
+    for b in range(W.B):
+        for h in range(W.Hq):
+            lens = None if w["lens"] is None else w["lens"][b:b + 1]
+            oracle.attention_backward(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1],
+                                      v[b:b + 1, h // G:h // G + 1], do[b:b + 1, h:h + 1], W.scale, W.causal, lens)
+            done += 10 * W.D * prefill_pairs(1, 1, W.Tq, W.Tk, W.causal, lens)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=done / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+                sample=f"gradients of {heads} of {W.B * W.Hq} (batch, head) pairs of the {W.name} workload, "
+                       f"float64 numpy, {dt:.1f} s")
 
 
 def setup_decode(torch):
@@ -307,6 +367,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="causal", choices=["causal", "long", "ragged", "decode", "single"])
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement of the default run")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the gradients (attn_bwd) of the prefill workload instead of its forward")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -357,6 +420,26 @@ def main():
         print(json.dumps(line), flush=True)
         return
 
+    if args.backward:
+        bw = setup_backward(torch, args.workload)
+        runner = Graphed(torch, bw["step"])
+        check_graph_replay(torch, runner, bw["step"], bw["out"])
+        ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
+        W = bw["W"]
+        tflops = bw["flops"] / (ms * 1e-3) / 1e12
+        line = dict(metric="prefill backward TFLOP/s (% bf16 MFMA peak)", value=round(tflops, 3), unit="TFLOP/s",
+                    n_gpus=1, steps=n, warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True,
+                    scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
+                    config=dict(workload=W.note + " (gradients)", B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk,
+                                D=W.D, causal=W.causal, flops_per_step=bw["flops"], parallelism="single GPU"),
+                    roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                                  frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                                  kernels="bwd_prep + bwd_dq + bwd_dkdv", kernel_ms=round(ms, 5)))
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_backward(args.workload, args.cpu_budget)
+        print(json.dumps(line), flush=True)
+        return
+
     pre = setup_prefill(torch, args.workload)
     runner = Graphed(torch, pre["step"])
     check_graph_replay(torch, runner, pre["step"], pre["out"])
@@ -394,6 +477,19 @@ def main():
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget / 2)
         del dec, drun
+    if args.workload == "causal" and not args.no_backward:
+        torch.cuda.empty_cache()
+        bw = setup_backward(torch, "causal")
+        brun = Graphed(torch, bw["step"])
+        check_graph_replay(torch, brun, bw["step"], bw["out"])
+        bms, bwall, bn = time_steps(torch, brun, max(20, args.steps // 4), max(5, args.warmup // 4))
+        btf = bw["flops"] / (bms * 1e-3) / 1e12
+        line["backward"] = dict(workload=bw["W"].note + " (gradients dQ, dK, dV)", value=round(btf, 3),
+                                unit="TFLOP/s", steps=bn, ms_per_step=round(bms, 5), flops_per_step=bw["flops"],
+                                roofline=dict(bound="mfma", achieved=round(btf, 3), peak=PEAK_BF16_TFLOPS,
+                                              unit="TFLOP/s", frac=round(btf / PEAK_BF16_TFLOPS, 4), traffic=None,
+                                              kernels="bwd_prep + bwd_dq + bwd_dkdv"))
+        del bw, brun
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(args.workload, args.cpu_budget)
     print(json.dumps(line), flush=True)
