@@ -13,6 +13,8 @@ Contents
 ``attention_rows``   the same definition evaluated one (b, h, i) row at a time,
                      for sampled checks at sizes the dense form cannot reach.
 ``decode``           one new query per sequence against a contiguous KV cache.
+``decode_paged``     the same step with the cache held in pages of a pool and
+                     found through a per-sequence block table.
 ``tiled_attention``  the tile-by-tile online-softmax algorithm (running max and
                      denominator, earlier partials rescaled), step by step.
 ``attention_backward``  dQ, dK, dV of sum(dO * O) by the chain rule through the
@@ -26,9 +28,9 @@ inputs).  No page prints output values for the seeded workloads, so the
 seeded outputs themselves are pinned only through those properties.
 """
 
-from .attention import attention, attention_rows, decode, valid_lengths
+from .attention import attention, attention_rows, decode, decode_paged, valid_lengths
 from .backward import attention_backward, backward_rows
 from .tiled import tiled_attention
 
-__all__ = ["attention", "attention_rows", "attention_backward", "backward_rows", "decode", "valid_lengths",
-           "tiled_attention"]
+__all__ = ["attention", "attention_rows", "attention_backward", "backward_rows", "decode", "decode_paged",
+           "valid_lengths", "tiled_attention"]

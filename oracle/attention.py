@@ -194,3 +194,36 @@ def decode(q, k_cache, v_cache, kv_lens, scale: float, batches=None):
             o[b, hk * G : (hk + 1) * G] = (p @ vv) / l
             lse[b, hk * G : (hk + 1) * G] = (m + np.log(l))[:, 0]
     return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale: float, batches=None):
+    """The decode step of ``decode`` over a paged cache.
+
+    The per-sequence cache is held in fixed-size pages of one pool (the
+    PagedAttention layout named in the introduction of "Implementing attention
+    from scratch"): logical key j of sequence b and KV head hk is
+    ``k_pages[block_table[b, j // P], hk, j % P]`` with P the page size, and
+    the same for V.  The step itself is the decode definition above over the
+    logical keys 0 .. kv_lens[b] - 1 (clamped to the table's capacity).
+
+    q: (B, Hq, D); k_pages, v_pages: (num_pages, Hkv, P, D);
+    block_table: (B, max_blocks) ints.  Returns (o, lse) as ``decode``.
+    """
+    B, Hq, D = q.shape
+    _, Hkv, P, _ = k_pages.shape
+    bt = np.asarray(_as_f64(block_table)).astype(np.int64)
+    cap = bt.shape[1] * P
+    lens = np.asarray(_as_f64(kv_lens)).reshape(-1).astype(np.int64)
+    o = np.zeros((B, Hq, D), dtype=np.float64)
+    lse = np.full((B, Hq), -np.inf, dtype=np.float64)
+    for b in range(B) if batches is None else batches:
+        L = int(min(max(lens[b], 0), cap))
+        if L == 0:
+            continue
+        j = np.arange(L)
+        pages, rows = bt[b, j // P], j % P
+        kk = np.stack([_as_f64(k_pages[pages, hk, rows]) for hk in range(Hkv)])[None]   # (1, Hkv, L, D)
+        vv = np.stack([_as_f64(v_pages[pages, hk, rows]) for hk in range(Hkv)])[None]
+        ob, lb = decode(_as_f64(q[b:b + 1]), kk, vv, [L], scale)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse

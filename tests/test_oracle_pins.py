@@ -366,3 +366,46 @@ def test_float64_random_shapes_against_sdpa_is_about_1e_10():
         ref = torch.nn.functional.scaled_dot_product_attention(
             torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True)
         assert np.abs(o - ref.numpy()).max() < gold["max_abs_error_below"]
+
+
+# ------------------------------------------------------------------ paged decode
+def _pool_from_cache(k, P):
+    """Pages holding a contiguous cache in order: page b*nb + i = rows i*P.. of sequence b."""
+    B, Hkv, S, D = k.shape
+    nb = S // P
+    return k.reshape(B, Hkv, nb, P, D).transpose(0, 2, 1, 3, 4).reshape(B * nb, Hkv, P, D)
+
+
+@pytest.mark.parametrize("P", [1, 4, 16])
+def test_paged_decode_identity_layout_equals_contiguous(P):
+    """Pages laid out in cache order with the identity table reduce to the
+    contiguous decode exactly."""
+    rng = np.random.default_rng(40)
+    B, Hq, Hkv, S, D = 3, 4, 2, 32, 8
+    q, k, v = rng.standard_normal((B, Hq, D)), rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    lens = [32, 1, 17]
+    nb = S // P
+    bt = np.arange(B * nb).reshape(B, nb)
+    o1, l1 = oracle.decode(q, k, v, lens, 0.3)
+    o2, l2 = oracle.decode_paged(q, _pool_from_cache(k, P), _pool_from_cache(v, P), bt, lens, 0.3)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_paged_decode_is_invariant_to_page_placement():
+    """Moving pages around the pool (and the table with them) and filling
+    unreferenced pages with NaN changes nothing."""
+    rng = np.random.default_rng(41)
+    B, Hq, Hkv, S, D, P = 2, 4, 1, 48, 8, 8
+    q, k, v = rng.standard_normal((B, Hq, D)), rng.standard_normal((B, Hkv, S, D)), rng.standard_normal((B, Hkv, S, D))
+    lens = [41, 48]
+    kp, vp = _pool_from_cache(k, P), _pool_from_cache(v, P)
+    nb = S // P
+    bt = np.arange(B * nb).reshape(B, nb)
+    o1, l1 = oracle.decode_paged(q, kp, vp, bt, lens, 0.5)
+    perm = rng.permutation(B * nb + 5)          # 5 extra, unreferenced pages
+    kp2 = np.full((B * nb + 5, Hkv, P, D), np.nan)
+    vp2 = np.full_like(kp2, np.nan)
+    kp2[perm[:B * nb]] = kp
+    vp2[perm[:B * nb]] = vp
+    o2, l2 = oracle.decode_paged(q, kp2, vp2, perm[bt], lens, 0.5)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
