@@ -224,6 +224,41 @@ def setup_decode(torch):
                 out=(o, lse))
 
 
+def setup_decode_paged(torch, page_size):
+    """The decode workload with its cache moved into a pool of pages placed at
+    random (same logical contents, so the same algorithmic bytes)."""
+    import exact_tiled_attention_13_amd as ea
+
+    dec = setup_decode(torch)
+    W, w = dec["W"], dec["w"]
+    k, v = w["k"], w["v"]
+    B, Hkv, S, D = k.shape
+    if S % page_size:
+        raise SystemExit("page size must divide the cache length")
+    nb = S // page_size
+    g = torch.Generator(device="cuda").manual_seed(2)
+    perm = torch.randperm(B * nb, generator=g, device="cuda")
+    kp = torch.empty((B * nb, Hkv, page_size, D), dtype=k.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    kp[perm] = k.reshape(B, Hkv, nb, page_size, D).transpose(1, 2).reshape(B * nb, Hkv, page_size, D)
+    vp[perm] = v.reshape(B, Hkv, nb, page_size, D).transpose(1, 2).reshape(B * nb, Hkv, page_size, D)
+    bt = perm.to(torch.int32).reshape(B, nb).contiguous()
+    q, kv = w["q"], w["kv_lens"]
+    o, lse = dec["out"]
+    ws = dec["keep"][-1]
+    del dec, k, v
+    w["k"] = w["v"] = None
+    torch.cuda.empty_cache()
+    args = (q.data_ptr(), kp.data_ptr(), vp.data_ptr(), bt.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq,
+            W.Hkv, B * nb, page_size, nb, W.D, W.scale, kv.data_ptr(), ws.data_ptr(), ws.numel(), ea.MIATTN_BF16)
+
+    def step():
+        ea.attn_decode_paged(*args, torch.cuda.current_stream().cuda_stream)
+
+    return dict(w=w, W=W, step=step, bytes=decode_bytes(W, w["lens"]), keep=(q, kp, vp, bt, kv, o, lse, ws),
+                out=(o, lse))
+
+
 def check_graph_replay(torch, runner, step, out):
     """Graph replays must reproduce an eager call bit for bit."""
     step()
@@ -365,7 +400,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="causal", choices=["causal", "long", "ragged", "decode", "single"])
+    ap.add_argument("--workload", default="causal",
+                    choices=["causal", "long", "ragged", "decode", "decode-paged", "single"])
+    ap.add_argument("--page-size", type=int, default=16, help="page size of --workload decode-paged")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement of the default run")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (attn_bwd) of the prefill workload instead of its forward")
@@ -399,23 +436,25 @@ def main():
     torch.cuda.set_device(0)
 
     line = {}
-    if args.workload == "decode":
-        dec = setup_decode(torch)
+    if args.workload in ("decode", "decode-paged"):
+        paged = args.workload == "decode-paged"
+        dec = setup_decode_paged(torch, args.page_size) if paged else setup_decode(torch)
         runner = Graphed(torch, dec["step"])
         check_graph_replay(torch, runner, dec["step"], dec["out"])
         ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
         gbs = dec["bytes"] / (ms * 1e-3) / 1e9
         W = dec["W"]
+        note = W.note + (f", paged cache (page size {args.page_size}, pages placed at random)" if paged else "")
         line = dict(metric="decode KV GB/s (% HBM peak)", value=round(gbs, 2), unit="GB/s", n_gpus=1, steps=n,
                     warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak",
                     vs_baseline=None, dtype="bf16", data="synthetic",
-                    config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
+                    config=dict(workload=note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
                                 sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU"),
                     roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                   frac=round(gbs / PEAK_HBM_GBS, 4),
-                                  traffic=traffic_for("decode_split_kernel", "decode"),
+                                  traffic=None if paged else traffic_for("decode_split_kernel", "decode"),
                                   kernels="decode_split + decode_merge"))
-        if not args.no_cpu_baseline:
+        if not args.no_cpu_baseline and not paged:
             line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
         print(json.dumps(line), flush=True)
         return

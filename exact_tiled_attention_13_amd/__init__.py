@@ -6,10 +6,11 @@ device memory and the current stream only.
 
     o, lse = fwd(q, k, v, causal=True)                 # prefill
     o, lse = decode(q, k_cache, v_cache, kv_lens)      # one KV-cache decode step
+    o, lse = decode_paged(q, k_pages, v_pages, block_table, kv_lens)   # paged cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True) # gradients of the prefill
 
 The C-ABI functions are re-exported under their C names (``attn_fwd``,
-``attn_decode``, ``attn_decode_workspace_size``, ``attn_bwd``,
+``attn_decode``, ``attn_decode_paged``, ``attn_decode_workspace_size``, ``attn_bwd``,
 ``attn_bwd_workspace_size``, ``attn_strerror``).
 """
 
@@ -27,13 +28,15 @@ from ._lib import (  # noqa: F401
     attn_bwd,
     attn_bwd_workspace_size,
     attn_decode,
+    attn_decode_paged,
     attn_decode_workspace_size,
     attn_fwd,
     attn_strerror,
     load,
 )
 
-__all__ = ["fwd", "decode", "bwd", "attn_fwd", "attn_decode", "attn_decode_workspace_size", "attn_bwd",
+__all__ = ["fwd", "decode", "decode_paged", "bwd", "attn_fwd", "attn_decode", "attn_decode_paged",
+           "attn_decode_workspace_size", "attn_bwd",
            "attn_bwd_workspace_size", "attn_strerror", "MiattnError", "load"]
 
 
@@ -133,6 +136,44 @@ def decode(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, workspac
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv,
                 S_max, D, scale, lens.data_ptr(), ws_ptr, ws_bytes, dt, stream)
+    return o, l_out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, kv_lens, *, scale: float | None = None, workspace=None, out=None,
+                 lse=None):
+    """One decode step against a paged cache.  q (B,Hq,D) bf16; k_pages / v_pages (num_pages,Hkv,page_size,D)
+    bf16; block_table int32 (B, max_blocks); kv_lens int32 (B,); all on the GPU.
+
+    Logical key j of sequence b is row j % page_size of page block_table[b, j // page_size].
+    Returns (o (B,Hq,D), lse (B,Hq) float32).
+    """
+    torch = _torch()
+    if q.dtype != torch.bfloat16:
+        raise ValueError("decode_paged takes bfloat16 tensors")
+    B, Hq, D = q.shape
+    _check_tensor("q", q, 3, q.dtype, q.device)
+    _check_tensor("k_pages", k_pages, 4, q.dtype, q.device)
+    _check_tensor("v_pages", v_pages, 4, q.dtype, q.device)
+    if k_pages.shape != v_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("page pool shapes do not match q")
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 (B, max_blocks)")
+    if block_table.device != q.device or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous tensor on the GPU of q")
+    max_blocks = block_table.shape[1]
+    lens = _lens(kv_lens, B, q.device, True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = attn_decode_workspace_size(B, Hq, Hkv, max_blocks * page_size, D)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q) if out is None else out
+    l_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(), o.data_ptr(),
+                      l_out.data_ptr(), B, Hq, Hkv, num_pages, page_size, max_blocks, D, scale, lens.data_ptr(),
+                      workspace.data_ptr(), workspace.numel() * workspace.element_size(), MIATTN_BF16, stream)
     return o, l_out
 
 

@@ -13,8 +13,8 @@ LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_PKG, "libmiattn.so")
 MIATTN_F32 = 0
 MIATTN_BF16 = 1
 
-EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_bwd_workspace_size", "attn_bwd",
-            "attn_strerror", "attn_abi_version")
+EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_bwd_workspace_size",
+            "attn_bwd", "attn_strerror", "attn_abi_version")
 
 _lib = None
 
@@ -44,6 +44,8 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, i, vp]
     lib.attn_decode.restype = i
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, sz, i, vp]
+    lib.attn_decode_paged.restype = i
     lib.attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, sz, i, vp]
@@ -100,4 +102,13 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, D, scale, ca
     code = load().attn_bwd(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
                            dk or None, dv or None, B, Hq, Hkv, Tq, Tk, D, float(scale), int(causal),
                            kv_lens or None, workspace or None, workspace_bytes, dtype, stream or None)
+    return _check(code) if check else code
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, o, lse, B, Hq, Hkv, num_pages, page_size, max_blocks, D,
+                      scale, kv_lens, workspace, workspace_bytes, dtype, stream, check=True):
+    """Raw C-ABI call; pointers are integers (0 = NULL)."""
+    code = load().attn_decode_paged(q or None, k_pages or None, v_pages or None, block_table or None, o or None,
+                                    lse or None, B, Hq, Hkv, num_pages, page_size, max_blocks, D, float(scale),
+                                    kv_lens or None, workspace or None, workspace_bytes, dtype, stream or None)
     return _check(code) if check else code

@@ -94,8 +94,37 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
   if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
   float* ws = static_cast<float*>(workspace);
   const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
-  miattn::DecodeArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D};
+  miattn::DecodeArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D,
+                       nullptr, 0, 0, 0};
   hipError_t e = miattn::launch_decode_bf16(a, st);
+  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+}
+
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,
+                      float* lse, int B, int Hq, int Hkv, int num_pages, int page_size, int max_blocks, int D,
+                      float scale, const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype,
+                      void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || max_blocks <= 0 || D <= 0 || Hq % Hkv != 0 ||
+      !std::isfinite(scale))
+    return MIATTN_ERR_SHAPE;
+  if (page_size < 8 || page_size > 65536 || (page_size & (page_size - 1)) != 0) return MIATTN_ERR_UNSUPPORTED;
+  if (!supported_d(D) || dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  // logical capacity of a sequence, and rows addressed in the pool
+  const long long cap = (long long)max_blocks * page_size;
+  if (cap > 0x7fffffffLL || (long long)num_pages * Hkv * page_size > (1LL << 40)) return MIATTN_ERR_SHAPE;
+  const int S_max = (int)cap;
+  const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
+  if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
+  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
+  float* ws = static_cast<float*>(workspace);
+  const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
+  miattn::DecodeArgs a{q, k_pages, v_pages, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D,
+                       block_table, shift, num_pages, max_blocks};
+  hipError_t e = miattn::launch_decode_bf16(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : hip_fail(e);
 }
 

@@ -113,11 +113,18 @@ __device__ __forceinline__ bool find_item(int t, const int32_t* __restrict__ kv_
 // Persistent split kernel: the grid is sized to the chip (two workgroups per
 // CU) and wave W takes items W, W + #waves, ...; the next tile, including
 // the first tile of the wave's next item, is always in flight.
-template <int D>
+//
+// Paged cache (PAGED): the rows of a sequence live in fixed-size pages of a
+// shared pool, found through its block table.  A work item covers 512
+// consecutive keys, i.e. at most 64 pages of >= 8 rows, so the wave loads
+// the item's page numbers once (one per lane) and every row address takes
+// its page from that vector with a lane shuffle.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
     const u16* __restrict__ Qd, const u16* __restrict__ Kc, const u16* __restrict__ Vc,
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
-    int B, int Hq, int Hkv, int S_max, int NS, int NHB, float c, int negq) {
+    int B, int Hq, int Hkv, int S_max, int NS, int NHB, float c, int negq,
+    const int32_t* __restrict__ block_table, int lgP, int num_pages, int max_blocks) {
   constexpr int KSTEPS = D / 32;             // k-steps of K Q^T
   constexpr int DB = D / 16;                 // 16-wide blocks of the head dim
   constexpr int TILE = kBN * D;              // elements per V tile
@@ -160,16 +167,33 @@ __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
   // key 16 kb + j, d 32 ks + 8 g .. +7) and the V rows into LDS stage BUF.
   // Keys at or past k1 are replaced by key k1-1 (finite data; masked below).
   u32x4 kf[2][2][KSTEPS];
+  // page numbers of the item being issued (lane i: its i-th page), paged only
+  int pvec = 0;
+  // element offset of logical key `key` of item `it` in the K and V arrays
+  auto row_off = [&](const DecItem& it, int key) -> size_t {
+    if constexpr (PAGED) {
+      const int page = __shfl(pvec, (key >> lgP) - (it.k0 >> lgP));
+      return ((((size_t)page * Hkv + it.hkv) << lgP) + (key & ((1 << lgP) - 1))) * D;
+    } else {
+      return (((size_t)it.b * Hkv + it.hkv) * (size_t)S_max + key) * D;
+    }
+  };
   auto issue = [&](auto BUF, const DecItem& it, int tile) {
     constexpr int buf = decltype(BUF)::value;
-    const size_t slab = ((size_t)it.b * Hkv + it.hkv) * (size_t)S_max * D;
-    const u16* Kp = Kc + slab;
-    const u16* Vp = Vc + slab;
+    if constexpr (PAGED) {
+      if (tile == 0) {
+        // the item's pages; out-of-range numbers are clamped into the pool
+        // (a wrong table gives wrong results, never a stray access)
+        const int blk = (it.k0 >> lgP) + lane;
+        const int p = blk < max_blocks ? block_table[(size_t)it.b * max_blocks + blk] : 0;
+        pvec = clampi(p, 0, num_pages - 1);
+      }
+    }
     const int kt = it.k0 + tile * kBN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = min(kt + 16 * kb + j, it.k1 - 1);
-      const u32x4* src = reinterpret_cast<const u32x4*>(Kp + (size_t)key * D + 8 * g);
+      const u32x4* src = reinterpret_cast<const u32x4*>(Kc + row_off(it, key) + 8 * g);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) kf[buf][kb][ks] = src[4 * ks];
     }
@@ -179,7 +203,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
       const int r = e / D, slot = (e % D) / 8;
       const int ch = slot ^ swz_v<D>(r);
       const int key = min(kt + r, it.k1 - 1);
-      __builtin_amdgcn_global_load_lds((gptr_t*)(Vp + (size_t)key * D + ch * 8),
+      __builtin_amdgcn_global_load_lds((gptr_t*)(Vc + row_off(it, key) + ch * 8),
                                        (lptr_t*)&Vs[w][buf][li * 512], 16, 0, kNonTemporal);
     }
   };
@@ -364,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   }
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const int NS = decode_num_splits(a.S_max);
   const int G = a.Hq / a.Hkv;
@@ -374,9 +398,9 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   // two workgroups (8 waves) per CU, never more waves than work items
   const long long items = (long long)a.B * NS * a.Hkv * NHB;
   const long long wgs = std::min<long long>(2LL * device_cu_count(), (items + kNW - 1) / kNW);
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3((unsigned)wgs), dim3(64 * kNW), 0, st, (const u16*)a.q,
+  hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3((unsigned)wgs), dim3(64 * kNW), 0, st, (const u16*)a.q,
                      (const u16*)a.k_cache, (const u16*)a.v_cache, a.kv_lens, a.ws_o, a.ws_ml, a.B, a.Hq, a.Hkv,
-                     a.S_max, NS, NHB, c, negq);
+                     a.S_max, NS, NHB, c, negq, a.block_table, a.page_shift, a.num_pages, a.max_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3((unsigned)a.Hq, (unsigned)a.B), dim3(256), 0, st, a.ws_o,
@@ -387,7 +411,8 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st) {
-  return a.D == 64 ? launch<64>(a, st) : launch<128>(a, st);
+  if (a.block_table != nullptr) return a.D == 64 ? launch<64, true>(a, st) : launch<128, true>(a, st);
+  return a.D == 64 ? launch<64, false>(a, st) : launch<128, false>(a, st);
 }
 
 }  // namespace miattn

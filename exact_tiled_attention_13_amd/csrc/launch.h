@@ -31,6 +31,12 @@ struct DecodeArgs {
   float scale;
   float* ws_o;             // split partial outputs
   float* ws_ml;            // split partial (max, sum)
+  // paged cache (block_table non-null): k_cache / v_cache are pools of
+  // [num_pages, Hkv, 2^page_shift, D]; logical key j of sequence b is row
+  // j & (page - 1) of page block_table[b * max_blocks + (j >> page_shift)].
+  // S_max is then max_blocks << page_shift.
+  const int32_t* block_table;
+  int page_shift, num_pages, max_blocks;
 };
 
 struct BwdArgs {

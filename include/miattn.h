@@ -102,6 +102,30 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
                 int dtype, void* stream);
 
+/*
+ * One decode step against a paged KV cache: the per-sequence caches live in
+ * fixed-size pages of one shared pool, found through a block table (the
+ * PagedAttention layout that "Implementing attention from scratch" names in
+ * its introduction; the operation is its KV caching section's decode step).
+ * Same operation and kv_lens meaning as attn_decode; only where the rows
+ * live differs:
+ *   k_pages, v_pages  device pools [num_pages, Hkv, page_size, D] (dtype)
+ *   block_table       device int32 [B, max_blocks]: logical key j of
+ *                     sequence b (j < kv_lens[b]) is row j % page_size of
+ *                     page block_table[b * max_blocks + j / page_size].
+ * page_size must be a power of two in [8, 65536]; kv_lens[b] is clamped to
+ * [0, max_blocks * page_size].  Table entries the call reads (the blocks
+ * covering keys < kv_lens[b]) must be valid page numbers; out-of-range
+ * entries are clamped into [0, num_pages) on the device (wrong results, no
+ * stray access).  Pages not referenced may hold anything, NaN included.
+ * workspace: at least attn_decode_workspace_size(B, Hq, Hkv,
+ * max_blocks * page_size, D) bytes.  bf16 only.
+ */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,
+                      float* lse, int B, int Hq, int Hkv, int num_pages, int page_size, int max_blocks, int D,
+                      float scale, const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype,
+                      void* stream);
+
 /* Bytes of device workspace attn_bwd needs: 8 * B * Hq * Tq. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Tq);
 

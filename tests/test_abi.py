@@ -109,6 +109,20 @@ def test_bwd_validation(lib, args, code):
     assert ea.attn_bwd(**a, check=False) == code
 
 
+@pytest.mark.parametrize("args,code", [
+    (dict(block_table=0), -1), (dict(k_pages=0), -1), (dict(kv_lens=0), -1),
+    (dict(num_pages=0), -2), (dict(max_blocks=0), -2), (dict(Hq=5, Hkv=2), -2),
+    (dict(page_size=12), -3), (dict(page_size=4), -3), (dict(page_size=1 << 17), -3), (dict(dtype=0), -3),
+    (dict(D=32), -3), (dict(workspace=0), -4), (dict(workspace_bytes=10), -4),
+])
+def test_decode_paged_validation(lib, args, code):
+    a = dict(q=FAKE, k_pages=FAKE, v_pages=FAKE, block_table=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, num_pages=10,
+             page_size=16, max_blocks=4, D=128, scale=0.1, kv_lens=FAKE, workspace=FAKE, workspace_bytes=1 << 40,
+             dtype=1, stream=0)
+    a.update(args)
+    assert ea.attn_decode_paged(**a, check=False) == code
+
+
 def test_bwd_workspace_size(lib):
     assert ea.attn_bwd_workspace_size(4, 16, 1024) == 8 * 4 * 16 * 1024
     assert ea.attn_bwd_workspace_size(0, 16, 1024) == 0
