@@ -184,8 +184,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O
 }
 
 // ---------------------------------------------------------------- bwd_dq
+// (at most 256 registers: two waves per SIMD; left alone the compiler spends
+// AccVGPRs and runs one)
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dQ, int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, float scale, int negk) {
@@ -310,8 +312,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------- bwd_dkdv
+// (two waves per SIMD at D=64; at D=128 the K, V fragments and the dK, dV
+// accumulators alone take 192 registers per lane, so one)
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
