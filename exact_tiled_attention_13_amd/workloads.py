@@ -21,12 +21,19 @@ decode     KV-cache decode with GQA, B=64, Hq=32, Hkv=8, D=128, one query per
            sequence, cached lengths uniform in [1024, 32768], cache
            (B, Hkv, 32768, D) bf16.
 long       long-context causal prefill, B=1, H=32, T=32768, D=128, bf16.
+decode-fp8 the decode workload with q and the caches as E4M3 codes (FP8, one
+           scale per tensor).
 =========  ===================================================================
 
 bf16 tensors are drawn as float32 N(0,1) from a seeded ``torch.Generator``
 and rounded to bf16 (round-to-nearest-even, torch's ``.to``); the oracle is
 then given exactly those bf16 values.  Lengths come from
 ``numpy.random.default_rng(seed)``.
+
+E4M3 tensors are the same N(0,1) draws divided by a per-tensor scale chosen
+so that 6 standard deviations map to the largest code (6 / 448), clamped to
++-448 and rounded by torch's float8_e4m3fn cast; the tensor then stands for
+codes * scale, and the oracle decodes exactly those codes.
 """
 
 from __future__ import annotations
@@ -48,7 +55,7 @@ class Workload:
     Tq: int            # 1 for decode
     Tk: int            # S_max for decode
     D: int
-    dtype: str         # "f32" or "bf16"
+    dtype: str         # "f32", "bf16" or "e4m3"
     causal: bool
     lens: tuple | None = None   # (lo, hi, force_first_one) or None
     note: str = field(default="", compare=False)
@@ -69,7 +76,14 @@ WORKLOADS = {
                        "decode GQA B=64 Hq=32 Hkv=8 D=128, lengths U[1024,32768]"),
     "long": Workload("long", "fwd", 1, 32, 32, 32768, 32768, 128, "bf16", True, None,
                      "long causal prefill B=1 H=32 T=32768 D=128 bf16"),
+    "decode-fp8": Workload("decode-fp8", "decode", 64, 32, 8, 1, 32768, 128, "e4m3", True, (1024, 32768, False),
+                           "decode GQA B=64 Hq=32 Hkv=8 D=128, lengths U[1024,32768], E4M3 q/K/V"),
 }
+
+# Largest finite E4M3 magnitude, and the per-tensor scale of the synthetic
+# E4M3 inputs (a standard deviation of 1 spread over the code range).
+E4M3_MAX = 448.0
+E4M3_SCALE = 6.0 / E4M3_MAX
 
 
 def draw_lengths(B: int, lo: int, hi: int, force_first_one: bool = False, seed: int = 0) -> np.ndarray:
@@ -83,6 +97,12 @@ def draw_lengths(B: int, lo: int, hi: int, force_first_one: bool = False, seed: 
 def randn_bf16(shape, gen: torch.Generator, device="cpu") -> torch.Tensor:
     """float32 N(0,1) draws rounded to bf16."""
     return torch.randn(shape, generator=gen, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
+def randn_e4m3(shape, gen: torch.Generator, scale: float = E4M3_SCALE, device="cpu") -> torch.Tensor:
+    """E4M3 codes (torch.float8_e4m3fn) of float32 N(0,1) draws divided by ``scale``."""
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) / scale
+    return x.clamp_(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
 
 
 def make_fwd_inputs(B, Hq, Hkv, Tq, Tk, D, dtype="bf16", seed=0, device="cpu"):
@@ -135,6 +155,25 @@ def make_decode_inputs(B, Hq, Hkv, S_max, D, lens, seed=0, device="cpu", poison=
     return q, k, v
 
 
+def make_decode_inputs_fp8(B, Hq, Hkv, S_max, D, lens, seed=0, device="cpu", poison=False,
+                           scales=(E4M3_SCALE, E4M3_SCALE, E4M3_SCALE)):
+    """E4M3 q (B, Hq, D) and caches (B, Hkv, S_max, D) plus their scales
+    (q_scale, k_scale, v_scale); poisoned rows hold the NaN code 0x7f."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    qs, ks, vs = scales
+    q = randn_e4m3((B, Hq, D), g, qs, device)
+    k = torch.empty((B, Hkv, S_max, D), dtype=torch.float8_e4m3fn, device=device)
+    v = torch.empty((B, Hkv, S_max, D), dtype=torch.float8_e4m3fn, device=device)
+    for b in range(B):
+        k[b] = randn_e4m3((Hkv, S_max, D), g, ks, device)
+    for b in range(B):
+        v[b] = randn_e4m3((Hkv, S_max, D), g, vs, device)
+    if poison:
+        for t in (k, v):
+            poison_tail_(t.view(torch.uint8), lens, 0x7F)
+    return q, k, v, (qs, ks, vs)
+
+
 def make(name: str, seed: int = 0, device="cpu", poison=False):
     """Inputs for a named workload.
 
@@ -149,6 +188,8 @@ def make(name: str, seed: int = 0, device="cpu", poison=False):
     if name == "single":
         q, k, v = make_single(seed)
         q, k, v = q.to(device), k.to(device), v.to(device)
+    elif w.kind == "decode" and w.dtype == "e4m3":
+        q, k, v, fp8_scales = make_decode_inputs_fp8(w.B, w.Hq, w.Hkv, w.Tk, w.D, lens, seed, device, poison)
     elif w.kind == "decode":
         q, k, v = make_decode_inputs(w.B, w.Hq, w.Hkv, w.Tk, w.D, lens, seed, device, poison)
     else:
@@ -157,4 +198,7 @@ def make(name: str, seed: int = 0, device="cpu", poison=False):
             poison_tail_(k, lens)
             poison_tail_(v, lens)
     kv = None if lens is None else torch.from_numpy(lens).to(device)
-    return dict(q=q, k=k, v=v, kv_lens=kv, lens=lens, scale=w.scale, causal=w.causal, workload=w)
+    out = dict(q=q, k=k, v=v, kv_lens=kv, lens=lens, scale=w.scale, causal=w.causal, workload=w)
+    if w.dtype == "e4m3":
+        out["fp8_scales"] = fp8_scales
+    return out

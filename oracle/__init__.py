@@ -20,9 +20,13 @@ Contents
 ``attention_backward``  dQ, dK, dV of sum(dO * O) by the chain rule through the
                      definition (softmax Jacobian row by row), float64.
 ``backward_rows``    dQ of selected rows, for sampled checks at large sizes.
+``e4m3_decode``      value of 8-bit E4M3 codes, from the format's definition.
+``attention_fp8``, ``attention_rows_fp8``, ``decode_fp8``, ``decode_paged_fp8``
+                     the definitions above on E4M3 inputs with one scale per
+                     tensor (values = codes * scale).
 
-Parity status: every function above is pinned by tests/test_oracle_pins.py
-and tests/test_oracle_backward_pins.py
+Parity status: every function above is pinned by tests/test_oracle_pins.py,
+tests/test_oracle_backward_pins.py and tests/test_oracle_fp8_pins.py
 (closed forms, invariants, a textbook library routine and brute force on tiny
 inputs).  No page prints output values for the seeded workloads, so the
 seeded outputs themselves are pinned only through those properties.
@@ -30,7 +34,9 @@ seeded outputs themselves are pinned only through those properties.
 
 from .attention import attention, attention_rows, decode, decode_paged, valid_lengths
 from .backward import attention_backward, backward_rows
+from .fp8 import attention_fp8, attention_rows_fp8, decode_fp8, decode_paged_fp8, e4m3_decode
 from .tiled import tiled_attention
 
 __all__ = ["attention", "attention_rows", "attention_backward", "backward_rows", "decode", "decode_paged",
-           "valid_lengths", "tiled_attention"]
+           "valid_lengths", "tiled_attention", "e4m3_decode", "attention_fp8", "attention_rows_fp8", "decode_fp8",
+           "decode_paged_fp8"]
