@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload causal|long|ragged|decode|single] [--backward]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload causal|long|ragged|decode|decode-paged|decode-fp8|single] [--backward]
 
 A step is one pass of the hot path over one batch of synthetic, seeded input
 already resident in HBM.  The headline line measures the causal prefill
@@ -9,7 +10,8 @@ workload (B=4, H=16, T=1024, D=64, bf16) in TFLOP/s of algorithmic work
 (4*D flops per unmasked (query, key) pair); the same run also times one
 KV-cache decode step of the GQA decode workload (B=64, Hq=32, Hkv=8, D=128,
 lengths 1024..32768) in GB/s of algorithmic bytes (the K/V rows each sequence
-needs plus q, o, lse and lengths), reported under "decode", and the gradients
+needs plus q, o, lse and lengths), reported under "decode", the same step on
+E4M3 (FP8) q and caches under "decode_fp8", and the gradients
 of the causal workload (10*D flops per unmasked pair: the five products of
 the backward), reported under "backward".  Steps are
 replayed from a HIP graph (a fixed number of calls per graph) so that host
@@ -43,7 +45,7 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h"],
     "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
-    "decode_split_kernel": ["decode_bf16.hip", "device_common.h", "launch.h"],
+    "decode_split_kernel": ["decode.hip", "device_common.h", "launch.h"],
 }
 COPY_BYTES = 1 << 30          # size of the calibration copy
 
@@ -67,8 +69,10 @@ def prefill_pairs(B, Hq, Tq, Tk, causal, lens):
 
 
 def decode_bytes(W, lens, elem=2):
+    """Algorithmic bytes of one decode step: the K and V rows each sequence
+    needs and q (elem bytes per element), o (bf16), lse and the lengths."""
     kv = 2 * W.Hkv * W.D * elem * int(np.sum(np.clip(lens, 0, W.Tk)))
-    return kv + 2 * W.B * W.Hq * W.D * elem + W.B * W.Hq * 4 + W.B * 4
+    return kv + W.B * W.Hq * W.D * (elem + 2) + W.B * W.Hq * 4 + W.B * 4
 
 
 def blas_threads():
@@ -224,6 +228,29 @@ def setup_decode(torch):
                 out=(o, lse))
 
 
+def setup_decode_fp8(torch):
+    """The decode workload with q and the caches as E4M3 codes (one scale per tensor)."""
+    import exact_tiled_attention_13_amd as ea
+    from exact_tiled_attention_13_amd import workloads
+
+    w = workloads.make("decode-fp8", device="cuda")
+    W = w["workload"]
+    q, k, v, kv = w["q"], w["k"], w["v"], w["kv_lens"]
+    qs, ks, vs = w["fp8_scales"]
+    o = torch.empty((W.B, W.Hq, W.D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((W.B, W.Hq), dtype=torch.float32, device="cuda")
+    nbytes = ea.attn_decode_workspace_size(W.B, W.Hq, W.Hkv, W.Tk, W.D)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq, W.Hkv, W.Tk, W.D,
+            W.scale, qs, ks, vs, kv.data_ptr(), ws.data_ptr(), nbytes)
+
+    def step():
+        ea.attn_decode_fp8(*args, torch.cuda.current_stream().cuda_stream)
+
+    return dict(w=w, W=W, step=step, bytes=decode_bytes(W, w["lens"], elem=1), keep=(q, k, v, kv, o, lse, ws),
+                out=(o, lse))
+
+
 def setup_decode_paged(torch, page_size):
     """The decode workload with its cache moved into a pool of pages placed at
     random (same logical contents, so the same algorithmic bytes)."""
@@ -307,17 +334,25 @@ def cpu_baseline_decode(dec, budget_s):
     w, W = dec["w"], dec["W"]
     lens = w["lens"]
     qc = w["q"].cpu()
+    fp8 = W.dtype == "e4m3"
+    elem = 1 if fp8 else 2
     done, nb = 0, 0
     t0 = time.perf_counter()
     for b in range(W.B):
-        oracle.decode(qc, w["k"], w["v"], lens, W.scale, batches=[b])
-        done += 2 * W.Hkv * W.D * 2 * int(lens[b]) + 2 * W.Hq * W.D * 2 + W.Hq * 4 + 4
+        if fp8:
+            # the oracle decodes only the rows it reads, from the device cache
+            kb, vb = w["k"][b:b + 1].cpu(), w["v"][b:b + 1].cpu()
+            oracle.decode_fp8(qc[b:b + 1], kb, vb, lens[b:b + 1], *w["fp8_scales"], W.scale)
+        else:
+            oracle.decode(qc, w["k"], w["v"], lens, W.scale, batches=[b])
+        done += 2 * W.Hkv * W.D * elem * int(lens[b]) + W.Hq * W.D * (elem + 2) + W.Hq * 4 + 4
         nb += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return dict(value=done / dt / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle",
-                sample=f"{nb} of {W.B} sequences of the decode workload (cache slabs upcast to float64), {dt:.1f} s")
+                sample=f"{nb} of {W.B} sequences of the {W.name} workload (cache slabs upcast to float64), "
+                       f"{dt:.1f} s")
 
 
 def sources_hash(kernel):
@@ -401,9 +436,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="causal",
-                    choices=["causal", "long", "ragged", "decode", "decode-paged", "single"])
+                    choices=["causal", "long", "ragged", "decode", "decode-paged", "decode-fp8", "single"])
     ap.add_argument("--page-size", type=int, default=16, help="page size of --workload decode-paged")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement of the default run")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements of the default run")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (attn_bwd) of the prefill workload instead of its forward")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement of the default run")
@@ -436,9 +471,11 @@ def main():
     torch.cuda.set_device(0)
 
     line = {}
-    if args.workload in ("decode", "decode-paged"):
+    if args.workload in ("decode", "decode-paged", "decode-fp8"):
         paged = args.workload == "decode-paged"
-        dec = setup_decode_paged(torch, args.page_size) if paged else setup_decode(torch)
+        fp8 = args.workload == "decode-fp8"
+        dec = (setup_decode_paged(torch, args.page_size) if paged else
+               setup_decode_fp8(torch) if fp8 else setup_decode(torch))
         runner = Graphed(torch, dec["step"])
         check_graph_replay(torch, runner, dec["step"], dec["out"])
         ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
@@ -447,12 +484,12 @@ def main():
         note = W.note + (f", paged cache (page size {args.page_size}, pages placed at random)" if paged else "")
         line = dict(metric="decode KV GB/s (% HBM peak)", value=round(gbs, 2), unit="GB/s", n_gpus=1, steps=n,
                     warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak",
-                    vs_baseline=None, dtype="bf16", data="synthetic",
+                    vs_baseline=None, dtype="e4m3" if fp8 else "bf16", data="synthetic",
                     config=dict(workload=note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
                                 sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU"),
                     roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                   frac=round(gbs / PEAK_HBM_GBS, 4),
-                                  traffic=None if paged else traffic_for("decode_split_kernel", "decode"),
+                                  traffic=None if paged else traffic_for("decode_split_kernel", args.workload),
                                   kernels="decode_split + decode_merge"))
         if not args.no_cpu_baseline and not paged:
             line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
@@ -515,6 +552,21 @@ def main():
                                             kernels="decode_split + decode_merge"))
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget / 2)
+        del dec, drun
+        torch.cuda.empty_cache()
+        dec = setup_decode_fp8(torch)
+        drun = Graphed(torch, dec["step"])
+        check_graph_replay(torch, drun, dec["step"], dec["out"])
+        dms, dwall, dn = time_steps(torch, drun, max(20, args.steps // 4), max(5, args.warmup // 4))
+        gbs = dec["bytes"] / (dms * 1e-3) / 1e9
+        DW = dec["W"]
+        line["decode_fp8"] = dict(workload=DW.note, value=round(gbs, 2), unit="GB/s", steps=dn,
+                                  ms_per_step=round(dms, 5), bytes_per_step=dec["bytes"],
+                                  sum_lengths=int(np.sum(dec["w"]["lens"])), dtype="e4m3",
+                                  roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                                                frac=round(gbs / PEAK_HBM_GBS, 4),
+                                                traffic=traffic_for("decode_split_kernel", "decode-fp8"),
+                                                kernels="decode_split + decode_merge"))
         del dec, drun
     if args.workload == "causal" and not args.no_backward:
         torch.cuda.empty_cache()

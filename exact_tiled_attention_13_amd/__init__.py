@@ -7,10 +7,12 @@ device memory and the current stream only.
     o, lse = fwd(q, k, v, causal=True)                 # prefill
     o, lse = decode(q, k_cache, v_cache, kv_lens)      # one KV-cache decode step
     o, lse = decode_paged(q, k_pages, v_pages, block_table, kv_lens)   # paged cache
+    o, lse = decode_fp8(q8, k8, v8, kv_lens, q_scale=.., k_scale=.., v_scale=..)   # E4M3 cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True) # gradients of the prefill
 
 The C-ABI functions are re-exported under their C names (``attn_fwd``,
-``attn_decode``, ``attn_decode_paged``, ``attn_decode_workspace_size``, ``attn_bwd``,
+``attn_decode``, ``attn_decode_paged``, ``attn_decode_fp8``, ``attn_decode_paged_fp8``,
+``attn_decode_workspace_size``, ``attn_bwd``,
 ``attn_bwd_workspace_size``, ``attn_strerror``).
 """
 
@@ -28,14 +30,17 @@ from ._lib import (  # noqa: F401
     attn_bwd,
     attn_bwd_workspace_size,
     attn_decode,
+    attn_decode_fp8,
     attn_decode_paged,
+    attn_decode_paged_fp8,
     attn_decode_workspace_size,
     attn_fwd,
     attn_strerror,
     load,
 )
 
-__all__ = ["fwd", "decode", "decode_paged", "bwd", "attn_fwd", "attn_decode", "attn_decode_paged",
+__all__ = ["fwd", "decode", "decode_paged", "decode_fp8", "decode_paged_fp8", "bwd", "attn_fwd", "attn_decode",
+           "attn_decode_paged", "attn_decode_fp8", "attn_decode_paged_fp8",
            "attn_decode_workspace_size", "attn_bwd",
            "attn_bwd_workspace_size", "attn_strerror", "MiattnError", "load"]
 
@@ -176,6 +181,80 @@ def decode_paged(q, k_pages, v_pages, block_table, kv_lens, *, scale: float | No
                       workspace.data_ptr(), workspace.numel() * workspace.element_size(), MIATTN_BF16, stream)
     return o, l_out
 
+
+
+def _e4m3_bytes(name, t, ndim, device):
+    """Check an E4M3 tensor (torch.float8_e4m3fn or its uint8 codes)."""
+    torch = _torch()
+    if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+        raise ValueError(f"{name} must be float8_e4m3fn or uint8 E4M3 codes, got {t.dtype}")
+    _check_tensor(name, t, ndim, t.dtype, device)
+
+
+def decode_fp8(q, k_cache, v_cache, kv_lens, *, q_scale: float, k_scale: float, v_scale: float,
+               scale: float | None = None, workspace=None, out=None, lse=None):
+    """One decode step on an E4M3 cache.  q (B,Hq,D), caches (B,Hkv,S_max,D): float8_e4m3fn (or uint8
+    codes) on the GPU, each standing for its codes times its scale; kv_lens int32 (B,).
+
+    Scores are scale * (q_scale q).(k_scale k) and O = P (v_scale V).
+    Returns (o (B,Hq,D) bfloat16, lse (B,Hq) float32).
+    """
+    torch = _torch()
+    B, Hq, D = q.shape
+    _e4m3_bytes("q", q, 3, q.device)
+    _e4m3_bytes("k_cache", k_cache, 4, q.device)
+    _e4m3_bytes("v_cache", v_cache, 4, q.device)
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    lens = _lens(kv_lens, B, q.device, True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = attn_decode_workspace_size(B, Hq, Hkv, S_max, D)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq,
+                    Hkv, S_max, D, scale, q_scale, k_scale, v_scale, lens.data_ptr(), workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), stream)
+    return o, l_out
+
+
+def decode_paged_fp8(q, k_pages, v_pages, block_table, kv_lens, *, q_scale: float, k_scale: float,
+                     v_scale: float, scale: float | None = None, workspace=None, out=None, lse=None):
+    """decode_paged on E4M3 pools (num_pages,Hkv,page_size,D) with per-tensor scales, as decode_fp8.
+
+    Returns (o (B,Hq,D) bfloat16, lse (B,Hq) float32).
+    """
+    torch = _torch()
+    B, Hq, D = q.shape
+    _e4m3_bytes("q", q, 3, q.device)
+    _e4m3_bytes("k_pages", k_pages, 4, q.device)
+    _e4m3_bytes("v_pages", v_pages, 4, q.device)
+    if k_pages.shape != v_pages.shape or k_pages.shape[3] != D:
+        raise ValueError("page pool shapes do not match q")
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 (B, max_blocks)")
+    if block_table.device != q.device or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous tensor on the GPU of q")
+    max_blocks = block_table.shape[1]
+    lens = _lens(kv_lens, B, q.device, True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = attn_decode_workspace_size(B, Hq, Hkv, max_blocks * page_size, D)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l_out = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_decode_paged_fp8(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                          o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv, num_pages, page_size, max_blocks, D, scale,
+                          q_scale, k_scale, v_scale, lens.data_ptr(), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), stream)
+    return o, l_out
 
 def bwd(q, k, v, o, lse, do, *, causal: bool = False, kv_lens=None, scale: float | None = None, workspace=None,
         dq=None, dk=None, dv=None):

@@ -13,8 +13,8 @@ LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_PKG, "libmiattn.so")
 MIATTN_F32 = 0
 MIATTN_BF16 = 1
 
-EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_bwd_workspace_size",
-            "attn_bwd", "attn_strerror", "attn_abi_version")
+EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_decode_fp8",
+            "attn_decode_paged_fp8", "attn_bwd_workspace_size", "attn_bwd", "attn_strerror", "attn_abi_version")
 
 _lib = None
 
@@ -46,6 +46,10 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.restype = i
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, sz, i, vp]
     lib.attn_decode_paged.restype = i
+    lib.attn_decode_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp, vp, sz, vp]
+    lib.attn_decode_fp8.restype = i
+    lib.attn_decode_paged_fp8.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, f, f, f, vp, vp, sz, vp]
+    lib.attn_decode_paged_fp8.restype = i
     lib.attn_bwd_workspace_size.argtypes = [i, i, i]
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, sz, i, vp]
@@ -111,4 +115,24 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, o, lse, B, Hq, Hkv, num_
     code = load().attn_decode_paged(q or None, k_pages or None, v_pages or None, block_table or None, o or None,
                                     lse or None, B, Hq, Hkv, num_pages, page_size, max_blocks, D, float(scale),
                                     kv_lens or None, workspace or None, workspace_bytes, dtype, stream or None)
+    return _check(code) if check else code
+
+
+def attn_decode_fp8(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, D, scale, q_scale, k_scale, v_scale, kv_lens,
+                    workspace, workspace_bytes, stream, check=True):
+    """Raw C-ABI call; pointers are integers (0 = NULL)."""
+    code = load().attn_decode_fp8(q or None, k_cache or None, v_cache or None, o or None, lse or None, B, Hq, Hkv,
+                                  S_max, D, float(scale), float(q_scale), float(k_scale), float(v_scale),
+                                  kv_lens or None, workspace or None, workspace_bytes, stream or None)
+    return _check(code) if check else code
+
+
+def attn_decode_paged_fp8(q, k_pages, v_pages, block_table, o, lse, B, Hq, Hkv, num_pages, page_size, max_blocks,
+                          D, scale, q_scale, k_scale, v_scale, kv_lens, workspace, workspace_bytes, stream,
+                          check=True):
+    """Raw C-ABI call; pointers are integers (0 = NULL)."""
+    code = load().attn_decode_paged_fp8(q or None, k_pages or None, v_pages or None, block_table or None,
+                                        o or None, lse or None, B, Hq, Hkv, num_pages, page_size, max_blocks, D,
+                                        float(scale), float(q_scale), float(k_scale), float(v_scale),
+                                        kv_lens or None, workspace or None, workspace_bytes, stream or None)
     return _check(code) if check else code

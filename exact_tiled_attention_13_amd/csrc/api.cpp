@@ -39,7 +39,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 2; }
+int attn_abi_version(void) { return 3; }
 
 const char* attn_strerror(int code) {
   switch (code) {
@@ -73,6 +73,52 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int D) {
   return miattn::decode_ws_floats(B, Hq, S_max, D) * sizeof(float);
 }
 
+namespace {
+
+// Checks and launches shared by the four decode entry points.  Contiguous
+// caches pass block_table = NULL; E4M3 caches pass fp8 = 1 and their scales.
+int decode_common(const void* q, const void* k, const void* v, const int32_t* block_table, void* o, float* lse,
+                  int B, int Hq, int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, void* workspace,
+                  size_t workspace_bytes, int page_shift, int num_pages, int max_blocks, int fp8, float q_scale,
+                  float k_scale, float v_scale, void* stream) {
+  const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
+  if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
+  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
+  // work items (sequence, head block, split) are counted in int32
+  if ((long long)B * gy * miattn::decode_num_splits(S_max) > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
+  float* ws = static_cast<float*>(workspace);
+  const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + nsp * (D + 2));
+  miattn::DecodeArgs a{q,           k,          v,         o,          lse,   kv_lens, B,       Hq,
+                       Hkv,         S_max,      D,         scale,      ws,    ws + nsp * D, idx,
+                       block_table, page_shift, num_pages, max_blocks, fp8,   q_scale, k_scale, v_scale};
+  hipError_t e = miattn::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+}
+
+// Page-size and pool checks of the paged entry points; sets shift and S_max.
+int paged_geometry(int num_pages, int page_size, int max_blocks, int Hkv, int* shift, int* S_max) {
+  if (page_size < 8 || page_size > 65536 || (page_size & (page_size - 1)) != 0) return MIATTN_ERR_UNSUPPORTED;
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  // logical capacity of a sequence, and rows addressed in the pool
+  const long long cap = (long long)max_blocks * page_size;
+  if (cap > 0x7fffffffLL || (long long)num_pages * Hkv * page_size > (1LL << 40)) return MIATTN_ERR_SHAPE;
+  *shift = sh;
+  *S_max = (int)cap;
+  return MIATTN_OK;
+}
+
+// The scores are scale * (q_scale q).(k_scale k): the product must be finite.
+bool fp8_scales_ok(float scale, float q_scale, float k_scale, float v_scale) {
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale)) return false;
+  const double qk = (double)scale * q_scale * k_scale * 1.4426950408889634;
+  return std::isfinite((float)qk);
+}
+
+}  // namespace
+
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
                 int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, void* workspace,
                 size_t workspace_bytes, int dtype, void* stream) {
@@ -80,24 +126,27 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
   if (!supported_d(D) || (dtype != MIATTN_F32 && dtype != MIATTN_BF16)) return MIATTN_ERR_UNSUPPORTED;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (dtype == MIATTN_F32) {
     // one query row against the cache, bottom-right causal: exactly the decode step
     if ((long long)B * Hq > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
     miattn::FwdArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, 1, S_max, D, scale, 1};
-    hipError_t e = miattn::launch_fwd_f32(a, st);
+    hipError_t e = miattn::launch_fwd_f32(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MIATTN_OK : hip_fail(e);
   }
-  const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
-  if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
-  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
-  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
-  float* ws = static_cast<float*>(workspace);
-  const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
-  miattn::DecodeArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D,
-                       nullptr, 0, 0, 0};
-  hipError_t e = miattn::launch_decode_bf16(a, st);
-  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+  return decode_common(q, k_cache, v_cache, nullptr, o, lse, B, Hq, Hkv, S_max, D, scale, kv_lens, workspace,
+                       workspace_bytes, 0, 0, 0, 0, 1.f, 1.f, 1.f, stream);
+}
+
+int attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+                    int Hkv, int S_max, int D, float scale, float q_scale, float k_scale, float v_scale,
+                    const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale) ||
+      !fp8_scales_ok(scale, q_scale, k_scale, v_scale))
+    return MIATTN_ERR_SHAPE;
+  if (!supported_d(D)) return MIATTN_ERR_UNSUPPORTED;
+  return decode_common(q, k_cache, v_cache, nullptr, o, lse, B, Hq, Hkv, S_max, D, scale, kv_lens, workspace,
+                       workspace_bytes, 0, 0, 0, 1, q_scale, k_scale, v_scale, stream);
 }
 
 int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table, void* o,
@@ -108,24 +157,28 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || max_blocks <= 0 || D <= 0 || Hq % Hkv != 0 ||
       !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
-  if (page_size < 8 || page_size > 65536 || (page_size & (page_size - 1)) != 0) return MIATTN_ERR_UNSUPPORTED;
   if (!supported_d(D) || dtype != MIATTN_BF16) return MIATTN_ERR_UNSUPPORTED;
-  int shift = 0;
-  while ((1 << shift) < page_size) ++shift;
-  // logical capacity of a sequence, and rows addressed in the pool
-  const long long cap = (long long)max_blocks * page_size;
-  if (cap > 0x7fffffffLL || (long long)num_pages * Hkv * page_size > (1LL << 40)) return MIATTN_ERR_SHAPE;
-  const int S_max = (int)cap;
-  const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
-  if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
-  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
-  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
-  float* ws = static_cast<float*>(workspace);
-  const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
-  miattn::DecodeArgs a{q, k_pages, v_pages, o, lse, kv_lens, B, Hq, Hkv, S_max, D, scale, ws, ws + nsp * D,
-                       block_table, shift, num_pages, max_blocks};
-  hipError_t e = miattn::launch_decode_bf16(a, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+  int shift = 0, S_max = 0;
+  const int g = paged_geometry(num_pages, page_size, max_blocks, Hkv, &shift, &S_max);
+  if (g != MIATTN_OK) return g;
+  return decode_common(q, k_pages, v_pages, block_table, o, lse, B, Hq, Hkv, S_max, D, scale, kv_lens, workspace,
+                       workspace_bytes, shift, num_pages, max_blocks, 0, 1.f, 1.f, 1.f, stream);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                          void* o, float* lse, int B, int Hq, int Hkv, int num_pages, int page_size, int max_blocks,
+                          int D, float scale, float q_scale, float k_scale, float v_scale, const int32_t* kv_lens,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || max_blocks <= 0 || D <= 0 || Hq % Hkv != 0 ||
+      !std::isfinite(scale) || !fp8_scales_ok(scale, q_scale, k_scale, v_scale))
+    return MIATTN_ERR_SHAPE;
+  if (!supported_d(D)) return MIATTN_ERR_UNSUPPORTED;
+  int shift = 0, S_max = 0;
+  const int g = paged_geometry(num_pages, page_size, max_blocks, Hkv, &shift, &S_max);
+  if (g != MIATTN_OK) return g;
+  return decode_common(q, k_pages, v_pages, block_table, o, lse, B, Hq, Hkv, S_max, D, scale, kv_lens, workspace,
+                       workspace_bytes, shift, num_pages, max_blocks, 1, q_scale, k_scale, v_scale, stream);
 }
 
 size_t attn_bwd_workspace_size(int B, int Hq, int Tq) {

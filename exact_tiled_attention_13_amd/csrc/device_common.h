@@ -58,6 +58,30 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const u16* __restrict__ p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// Byte-transposing 8-byte LDS read (ds_read_b64_tr_b8).  Within each group of
+// 16 lanes, lane i receives byte i % 8 of the 8-byte chunks addressed by
+// lanes 2t + i / 8, t = 0..7, in that order: if lane 2t + u points at bytes
+// 8u .. 8u+7 of a row R_t, lane i gets column i of rows R_0 .. R_7.
+// Restrict-qualified for the same reason as lds_read_tr16.
+__device__ __forceinline__ u32x2 lds_read_tr8(const __attribute__((address_space(3))) uint8_t* __restrict__ p) {
+  i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Eight E4M3 codes (byte k of the pair = element k) to eight bf16 values.
+// Every E4M3 value is a bf16 value, so the conversion is exact; the scale
+// operand of the conversion is 1.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 x) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+  const uint32_t b = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+  const uint32_t c = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+  const uint32_t d = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+  return __builtin_bit_cast(bf16x8, u32x4{a, b, c, d});
+}
+
 // max(x[l], x[l^32]) and x[l] + x[l^32] across the two wave halves.
 __device__ __forceinline__ float xhalf_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

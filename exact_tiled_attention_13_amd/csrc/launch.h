@@ -31,12 +31,18 @@ struct DecodeArgs {
   float scale;
   float* ws_o;             // split partial outputs
   float* ws_ml;            // split partial (max, sum)
+  int32_t* ws_idx;         // [0]: work items; [1 + b]: splits before sequence b
   // paged cache (block_table non-null): k_cache / v_cache are pools of
   // [num_pages, Hkv, 2^page_shift, D]; logical key j of sequence b is row
   // j & (page - 1) of page block_table[b * max_blocks + (j >> page_shift)].
   // S_max is then max_blocks << page_shift.
   const int32_t* block_table;
   int page_shift, num_pages, max_blocks;
+  // E4M3 cache (fp8 non-zero): q, k_cache, v_cache hold E4M3 codes, each
+  // tensor standing for its codes times its scale; o stays bf16.  The
+  // bf16 path uses scales of 1.
+  int fp8;
+  float q_scale, k_scale, v_scale;
 };
 
 struct BwdArgs {
@@ -59,11 +65,16 @@ struct BwdArgs {
 inline size_t bwd_ws_floats(int B, int Hq, int Tq) { return 2 * (size_t)B * Hq * Tq; }
 
 // Keys handled by one decode split (one wave).
-constexpr int kDecodeSplitKeys = 512;
+#ifndef DEC_SPLIT_KEYS
+#define DEC_SPLIT_KEYS 512
+#endif
+constexpr int kDecodeSplitKeys = DEC_SPLIT_KEYS;
 
 inline int decode_num_splits(int S_max) { return (S_max + kDecodeSplitKeys - 1) / kDecodeSplitKeys; }
+// partial outputs and (max, sum) per (sequence, query head, split), then
+// B + 1 int32 of work-item bookkeeping
 inline size_t decode_ws_floats(int B, int Hq, int S_max, int D) {
-  return (size_t)B * Hq * decode_num_splits(S_max) * (size_t)(D + 2);
+  return (size_t)B * Hq * decode_num_splits(S_max) * (size_t)(D + 2) + (size_t)B + 1;
 }
 
 // Compute units of the current device (cached per device; 256 if unknown).
@@ -71,7 +82,7 @@ int device_cu_count();
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
-hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 
 }  // namespace miattn

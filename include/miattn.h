@@ -68,7 +68,7 @@ enum {
 enum {
   MIATTN_OK = 0,
   MIATTN_ERR_NULL = -1,        /* a required pointer is NULL */
-  MIATTN_ERR_SHAPE = -2,       /* size <= 0, Hq % Hkv != 0, non-finite scale, or grid too large */
+  MIATTN_ERR_SHAPE = -2,       /* size <= 0, Hq % Hkv != 0, non-finite scale(s), or grid too large */
   MIATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, causal not 0/1 */
   MIATTN_ERR_WORKSPACE = -4,   /* workspace missing or too small */
   MIATTN_ERR_HIP = -5          /* the HIP runtime refused a launch; see attn_strerror */
@@ -84,7 +84,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
              const int32_t* kv_lens, int dtype, void* stream);
 
-/* Bytes of device workspace attn_decode needs for these sizes (bf16 path). */
+/* Bytes of device workspace the decode calls need for these sizes (split
+ * partials plus a little bookkeeping; not used by the float32 path). */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int D);
 
 /*
@@ -125,6 +126,38 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
                       float* lse, int B, int Hq, int Hkv, int num_pages, int page_size, int max_blocks, int D,
                       float scale, const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype,
                       void* stream);
+
+/*
+ * Decode steps on caches of 8-bit floating-point codes (E4M3, the "fn"
+ * variant of the OCP 8-bit formats: 1 sign, 4 exponent bits with bias 7,
+ * 3 mantissa bits, no infinities, 0x7f/0xff NaN, largest magnitude 448),
+ * the FP8 inputs that the self-attention interview question ("Self-Attention:
+ * Implementation, Complexity ..."), Follow-up questions, lists among
+ * FlashAttention-3's additions.  q, k_cache / k_pages and
+ * v_cache / v_pages hold one code byte per element in the same layouts as
+ * attn_decode / attn_decode_paged; each tensor stands for its codes times its
+ * per-tensor scale (q_scale, k_scale, v_scale: finite, any sign), so the
+ * operation is attn_decode's with
+ *   scores = scale * (q_scale q) . (k_scale k),   O = P (v_scale V).
+ * o is bfloat16 [B, Hq, D]; lse (float32 [B, Hq] or NULL) is the natural-log
+ * LSE of those scores.  The scores are exact products of the codes summed in
+ * fp32; V is widened to bf16 exactly and P is rounded to bf16 as in the bf16
+ * path.  NaN codes past kv_lens[b] are never read into the result.
+ * workspace: attn_decode_workspace_size(...) bytes as for the bf16 calls
+ * (S_max = max_blocks * page_size for the paged one).  Other arguments,
+ * checks and errors as for attn_decode / attn_decode_paged;
+ * scale * q_scale * k_scale must be finite in float32 (else
+ * MIATTN_ERR_SHAPE).
+ */
+int attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                    int B, int Hq, int Hkv, int S_max, int D, float scale,
+                    float q_scale, float k_scale, float v_scale,
+                    const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream);
+
+int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                          void* o, float* lse, int B, int Hq, int Hkv, int num_pages, int page_size,
+                          int max_blocks, int D, float scale, float q_scale, float k_scale, float v_scale,
+                          const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace attn_bwd needs: 8 * B * Hq * Tq. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Tq);

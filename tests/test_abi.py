@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert ea.attn_abi_version() == 2
+    assert ea.attn_abi_version() == 3
 
 
 def test_strerror_covers_codes(lib):
@@ -87,11 +87,12 @@ def test_decode_validation(lib, args, code):
 
 
 def test_workspace_size(lib):
-    # one split per 512 keys; per (sequence, query head, split): D floats + max + sum
-    assert ea.attn_decode_workspace_size(64, 32, 8, 32768, 128) == 64 * 32 * 64 * 130 * 4
-    assert ea.attn_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4
-    assert ea.attn_decode_workspace_size(1, 1, 1, 512, 64) == 66 * 4
-    assert ea.attn_decode_workspace_size(1, 1, 1, 513, 64) == 2 * 66 * 4
+    # one split per 512 keys; per (sequence, query head, split): D floats + max + sum,
+    # then B + 1 int32 of work bookkeeping
+    assert ea.attn_decode_workspace_size(64, 32, 8, 32768, 128) == 64 * 32 * 64 * 130 * 4 + 65 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 1, 64) == 66 * 4 + 2 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 512, 64) == 66 * 4 + 2 * 4
+    assert ea.attn_decode_workspace_size(1, 1, 1, 513, 64) == 2 * 66 * 4 + 2 * 4
     assert ea.attn_decode_workspace_size(0, 1, 1, 1, 64) == 0
 
 
@@ -123,6 +124,35 @@ def test_decode_paged_validation(lib, args, code):
     assert ea.attn_decode_paged(**a, check=False) == code
 
 
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1), (dict(k_cache=0), -1), (dict(v_cache=0), -1), (dict(o=0), -1), (dict(kv_lens=0), -1),
+    (dict(B=0), -2), (dict(S_max=0), -2), (dict(Hq=5, Hkv=2), -2), (dict(scale=float("nan")), -2),
+    (dict(q_scale=float("inf")), -2), (dict(k_scale=float("nan")), -2), (dict(v_scale=float("inf")), -2),
+    (dict(scale=1e30, q_scale=1e10, k_scale=1e10), -2),          # the score factor overflows float32
+    (dict(D=32), -3), (dict(workspace=0), -4), (dict(workspace_bytes=10), -4),
+])
+def test_decode_fp8_validation(lib, args, code):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, S_max=100, D=128, scale=0.1,
+             q_scale=0.01, k_scale=0.02, v_scale=0.03, kv_lens=FAKE, workspace=FAKE, workspace_bytes=1 << 40,
+             stream=0)
+    a.update(args)
+    assert ea.attn_decode_fp8(**a, check=False) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(block_table=0), -1), (dict(v_pages=0), -1), (dict(kv_lens=0), -1),
+    (dict(num_pages=0), -2), (dict(max_blocks=0), -2), (dict(q_scale=float("nan")), -2),
+    (dict(page_size=12), -3), (dict(page_size=4), -3), (dict(D=96), -3),
+    (dict(workspace=0), -4), (dict(workspace_bytes=10), -4),
+])
+def test_decode_paged_fp8_validation(lib, args, code):
+    a = dict(q=FAKE, k_pages=FAKE, v_pages=FAKE, block_table=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, num_pages=10,
+             page_size=16, max_blocks=4, D=128, scale=0.1, q_scale=0.01, k_scale=0.02, v_scale=0.03,
+             kv_lens=FAKE, workspace=FAKE, workspace_bytes=1 << 40, stream=0)
+    a.update(args)
+    assert ea.attn_decode_paged_fp8(**a, check=False) == code
+
 def test_bwd_workspace_size(lib):
     assert ea.attn_bwd_workspace_size(4, 16, 1024) == 8 * 4 * 16 * 1024
     assert ea.attn_bwd_workspace_size(0, 16, 1024) == 0
@@ -136,3 +166,6 @@ def test_python_wrappers_reject_bad_tensors():
         ea.fwd(q, q, q)  # CPU tensors are refused before any library call
     with pytest.raises(ValueError):
         ea.fwd(q.half(), q.half(), q.half())
+
+    with pytest.raises(ValueError):
+        ea.decode_fp8(q[:, :, 0], q, q, None, q_scale=1.0, k_scale=1.0, v_scale=1.0)   # not E4M3
