@@ -5,12 +5,13 @@ The compute path is the HIP library ``libmiattn.so`` (C ABI in
 device memory and the current stream only.
 
     o, lse = fwd(q, k, v, causal=True)                 # prefill
+    o, lse = fwd_fp8(q8, k8, v8, q_scale=.., k_scale=.., v_scale=.., causal=True)   # E4M3 prefill
     o, lse = decode(q, k_cache, v_cache, kv_lens)      # one KV-cache decode step
     o, lse = decode_paged(q, k_pages, v_pages, block_table, kv_lens)   # paged cache
     o, lse = decode_fp8(q8, k8, v8, kv_lens, q_scale=.., k_scale=.., v_scale=..)   # E4M3 cache
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True) # gradients of the prefill
 
-The C-ABI functions are re-exported under their C names (``attn_fwd``,
+The C-ABI functions are re-exported under their C names (``attn_fwd``, ``attn_fwd_fp8``,
 ``attn_decode``, ``attn_decode_paged``, ``attn_decode_fp8``, ``attn_decode_paged_fp8``,
 ``attn_decode_workspace_size``, ``attn_bwd``,
 ``attn_bwd_workspace_size``, ``attn_strerror``).
@@ -35,12 +36,13 @@ from ._lib import (  # noqa: F401
     attn_decode_paged_fp8,
     attn_decode_workspace_size,
     attn_fwd,
+    attn_fwd_fp8,
     attn_strerror,
     load,
 )
 
-__all__ = ["fwd", "decode", "decode_paged", "decode_fp8", "decode_paged_fp8", "bwd", "attn_fwd", "attn_decode",
-           "attn_decode_paged", "attn_decode_fp8", "attn_decode_paged_fp8",
+__all__ = ["fwd", "fwd_fp8", "decode", "decode_paged", "decode_fp8", "decode_paged_fp8", "bwd", "attn_fwd", "attn_decode",
+           "attn_decode_paged", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_fwd_fp8",
            "attn_decode_workspace_size", "attn_bwd",
            "attn_bwd_workspace_size", "attn_strerror", "MiattnError", "load"]
 
@@ -190,6 +192,32 @@ def _e4m3_bytes(name, t, ndim, device):
         raise ValueError(f"{name} must be float8_e4m3fn or uint8 E4M3 codes, got {t.dtype}")
     _check_tensor(name, t, ndim, t.dtype, device)
 
+
+def fwd_fp8(q, k, v, *, q_scale: float, k_scale: float, v_scale: float, causal: bool = False, kv_lens=None,
+            scale: float | None = None, out=None, lse=None):
+    """Prefill on E4M3 inputs.  q (B,Hq,Tq,D), k/v (B,Hkv,Tk,D): float8_e4m3fn (or uint8 codes) on the GPU,
+    each standing for its codes times its scale.
+
+    Scores are scale * (q_scale q).(k_scale k) and O = P (v_scale V).
+    Returns (o (B,Hq,Tq,D) bfloat16, lse (B,Hq,Tq) float32).
+    """
+    torch = _torch()
+    B, Hq, Tq, D = q.shape
+    _e4m3_bytes("q", q, 4, q.device)
+    _e4m3_bytes("k", k, 4, q.device)
+    _e4m3_bytes("v", v, 4, q.device)
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv, Tk = k.shape[1], k.shape[2]
+    lens = _lens(kv_lens, B, q.device, False)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    o = torch.empty((B, Hq, Tq, D), dtype=torch.bfloat16, device=q.device) if out is None else out
+    l_out = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv, Tq, Tk, D,
+                 scale, q_scale, k_scale, v_scale, 1 if causal else 0, 0 if lens is None else lens.data_ptr(), stream)
+    return o, l_out
 
 def decode_fp8(q, k_cache, v_cache, kv_lens, *, q_scale: float, k_scale: float, v_scale: float,
                scale: float | None = None, workspace=None, out=None, lse=None):

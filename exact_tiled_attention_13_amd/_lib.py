@@ -13,7 +13,7 @@ LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_PKG, "libmiattn.so")
 MIATTN_F32 = 0
 MIATTN_BF16 = 1
 
-EXPORTED = ("attn_fwd", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_decode_fp8",
+EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_decode_fp8",
             "attn_decode_paged_fp8", "attn_bwd_workspace_size", "attn_bwd", "attn_strerror", "attn_abi_version")
 
 _lib = None
@@ -40,6 +40,8 @@ def load() -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, vp]
     lib.attn_fwd.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, f, f, f, i, vp, vp]
+    lib.attn_fwd_fp8.restype = i
     lib.attn_decode_workspace_size.argtypes = [i, i, i, i, i]
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, i, vp]
@@ -88,6 +90,15 @@ def attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, D, scale, causal, kv_lens, dty
     """Raw C-ABI call; pointers are integers (0 = NULL)."""
     code = load().attn_fwd(q or None, k or None, v or None, o or None, lse or None, B, Hq, Hkv, Tq, Tk, D,
                            float(scale), int(causal), kv_lens or None, dtype, stream or None)
+    return _check(code) if check else code
+
+
+def attn_fwd_fp8(q, k, v, o, lse, B, Hq, Hkv, Tq, Tk, D, scale, q_scale, k_scale, v_scale, causal, kv_lens, stream,
+                 check=True):
+    """Raw C-ABI call; pointers are integers (0 = NULL)."""
+    code = load().attn_fwd_fp8(q or None, k or None, v or None, o or None, lse or None, B, Hq, Hkv, Tq, Tk, D,
+                               float(scale), float(q_scale), float(k_scale), float(v_scale), int(causal),
+                               kv_lens or None, stream or None)
     return _check(code) if check else code
 
 

@@ -19,6 +19,13 @@ int hip_fail(hipError_t e) {
 
 bool supported_d(int D) { return D == 64 || D == 128; }
 
+// The scores are scale * (q_scale q).(k_scale k): the product must be finite.
+bool fp8_scales_ok(float scale, float q_scale, float k_scale, float v_scale) {
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale)) return false;
+  const double qk = (double)scale * q_scale * k_scale * 1.4426950408889634;
+  return std::isfinite((float)qk);
+}
+
 }  // namespace
 
 namespace miattn {
@@ -39,7 +46,7 @@ int device_cu_count() {
 
 extern "C" {
 
-int attn_abi_version(void) { return 3; }
+int attn_abi_version(void) { return 4; }
 
 const char* attn_strerror(int code) {
   switch (code) {
@@ -65,6 +72,20 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   miattn::FwdArgs a{q, k, v, o, lse, kv_lens, B, Hq, Hkv, Tq, Tk, D, scale, causal};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = dtype == MIATTN_BF16 ? miattn::launch_fwd_bf16(a, st) : miattn::launch_fwd_f32(a, st);
+  return e == hipSuccess ? MIATTN_OK : hip_fail(e);
+}
+
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Tq,
+                 int Tk, int D, float scale, float q_scale, float k_scale, float v_scale, int causal,
+                 const int32_t* kv_lens, void* stream) {
+  if (!q || !k || !v || !o) return MIATTN_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale) ||
+      !fp8_scales_ok(scale, q_scale, k_scale, v_scale))
+    return MIATTN_ERR_SHAPE;
+  if (!supported_d(D) || (causal != 0 && causal != 1)) return MIATTN_ERR_UNSUPPORTED;
+  if ((long long)((Tq + 127) / 128) * B * Hq > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
+  miattn::FwdArgs a{q, k, v, o, lse, kv_lens, B, Hq, Hkv, Tq, Tk, D, scale, causal, q_scale, k_scale, v_scale};
+  hipError_t e = miattn::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? MIATTN_OK : hip_fail(e);
 }
 
@@ -108,13 +129,6 @@ int paged_geometry(int num_pages, int page_size, int max_blocks, int Hkv, int* s
   *shift = sh;
   *S_max = (int)cap;
   return MIATTN_OK;
-}
-
-// The scores are scale * (q_scale q).(k_scale k): the product must be finite.
-bool fp8_scales_ok(float scale, float q_scale, float k_scale, float v_scale) {
-  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale)) return false;
-  const double qk = (double)scale * q_scale * k_scale * 1.4426950408889634;
-  return std::isfinite((float)qk);
 }
 
 }  // namespace

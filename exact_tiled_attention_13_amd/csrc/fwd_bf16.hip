@@ -58,28 +58,34 @@
 namespace miattn {
 namespace {
 
-template <int D, int NWG, int KSPLIT>
+template <int D, int NWG, int KSPLIT, bool FP8>
 struct FwdCfg {
   static constexpr int NW = NWG * KSPLIT;           // waves per workgroup
-  // keys per tile and LDS stages per key group (tiles in flight + 1).  One
-  // key group: 64-key tiles, 3-4 stages (64-96 KiB).  Two key groups: two
-  // stages each within 64 KiB in all, so that two workgroups share a CU.
+  // keys per tile and LDS stages per key group (tiles in flight + 1; E4M3
+  // keeps one more stage, whose V tile is being widened).  One key group:
+  // 64-key tiles, 3-4 stages (64-96 KiB).  Two key groups: two stages each
+  // within 64-80 KiB in all, so that two workgroups share a CU.
   static constexpr int BN = (KSPLIT > 1 && D == 128) ? 32 : 64;
-  static constexpr int NS = (KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3);
+  static constexpr int NS = ((KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3)) + (FP8 ? 1 : 0);
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int BM = 32 * NWG;               // query rows per workgroup
   static constexpr int NT = 64 * NW;                // threads per workgroup
-  static constexpr int KS = D / 16;                 // k-steps of Q K^T
+  static constexpr int KS = D / 16;                 // k-steps of Q K^T (bf16)
+  static constexpr int KK = D / 64;                 // k-steps of Q K^T (E4M3)
   static constexpr int DB = D / 32;                 // 32-wide blocks of the head dim
+  static constexpr int ESZ = FP8 ? 1 : 2;           // bytes per input element
   static constexpr int TILE = BN * D;               // elements per K or V tile
-  static constexpr int LOADS = TILE * 2 / 1024;     // 1 KiB wave-loads per tensor per tile
+  static constexpr int TB = TILE * ESZ;             // bytes per K or V tile in a stage
+  static constexpr int LOADS = TB / 1024;           // 1 KiB wave-loads per tensor per tile
   // every wave of a group issues the same number of copies (vmcnt
-  // accounting is per wave); when NWG does not divide LOADS some waves
+  // accounting is per wave); when NWG does not divide 2 LOADS some waves
   // repeat another wave's copy, which writes the same bytes to the same place
-  static constexpr int LOADS_PER_WAVE = (LOADS + NWG - 1) / NWG;
-  static constexpr int VMEM_PER_TILE = 2 * LOADS_PER_WAVE;
-  static constexpr int RING = NS * 2 * TILE;        // u16 elements per key group
+  static constexpr int VMEM_PER_TILE = (2 * LOADS + NWG - 1) / NWG;
+  static constexpr int VW_BYTES = FP8 ? 2 * TILE * 2 : 0;   // widened V tiles (bf16, two buffers)
+  static constexpr int RING_BYTES = NS * 2 * TB + VW_BYTES;
+  static constexpr int RING = RING_BYTES / 2;       // u16 elements per key group
   static constexpr int SMEM = KSPLIT * RING;
+  static constexpr int WE = TILE / (64 * NWG);      // V elements each thread widens per tile (E4M3)
   // merge through the (then idle) rings: the partial (m, l) of groups 1..,
   // then their accumulators, DBR blocks of 32 columns per round
   static constexpr int ML_FLOATS = (KSPLIT - 1) * NWG * 64 * 2;
@@ -88,6 +94,7 @@ struct FwdCfg {
   static constexpr int DBR = (DB * BLK_FLOATS <= AVAIL) ? DB : (DB % 2 == 0 && DB / 2 * BLK_FLOATS <= AVAIL) ? DB / 2 : 1;
   static_assert(KSPLIT == 1 || BLK_FLOATS <= AVAIL, "merge buffer must fit in the rings");
   static_assert(SMEM * 2 <= 160 * 1024, "LDS");
+  static_assert(!FP8 || WE == 8 || WE == 16, "widening granule");
 };
 
 constexpr float kThresh = 8.0f;
@@ -100,8 +107,15 @@ constexpr float kThresh = 8.0f;
 //   V (read as 4 rows x 4 chunks per 32 lanes):   D=128: 4 (r & 3); D=64: 4 ((r >> 1) & 1)
 template <int D>
 __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+// E4M3 K rows are D bytes (8 or 4 chunks); 16 consecutive rows x one chunk:
+//   D=128: (r >> 1) & 7;  D=64: (r >> 2) & 3
+template <int D>
+__device__ __forceinline__ int swz_k8(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// s_waitcnt lgkmcnt(0) only (vmcnt 63, expcnt 7)
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
 template <int N>
@@ -124,21 +138,27 @@ __device__ __forceinline__ void wait_tile(int rem) {
 typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
 typedef __attribute__((address_space(3))) const u16 lds_u16;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Hide a per-lane LDS base from loop-invariant code motion (an empty asm
 // that emits nothing), so that each group of fragment reads is one add plus
 // reads whose constant row offsets fold into the DS immediate.
-__device__ __forceinline__ lds_u16* lds_base(lds_u16* p) {
+template <typename P>
+__device__ __forceinline__ P* lds_base(P* p) {
   asm volatile("" : "+v"(p));
   return p;
 }
 
-template <int D, int NWG, int KSPLIT, bool CAUSAL>
+template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
 __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V,
+    const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
-    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int zig) {
-  using C = FwdCfg<D, NWG, KSPLIT>;
+    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int zig, float oscale) {
+  using C = FwdCfg<D, NWG, KSPLIT, FP8>;
+  const uint8_t* __restrict__ Q = static_cast<const uint8_t*>(Qv);
+  const uint8_t* __restrict__ K = static_cast<const uint8_t*>(Kv);
+  const uint8_t* __restrict__ V = static_cast<const uint8_t*>(Vv);
   __shared__ __attribute__((aligned(1024))) u16 smem[C::SMEM];   // [key group][stage][K, V][tile]
 
   const int tid = threadIdx.x;
@@ -171,9 +191,10 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   const int off = Lk - Lq;  // bottom-right causal alignment
   const int q0 = qt * C::BM;
 
-  const u16* Qp = Q + ((size_t)b * Hq + hq) * (size_t)Tq * D;
-  const u16* Kp = K + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
-  const u16* Vp = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+  // byte addresses of this head's rows
+  const uint8_t* Qp = Q + ((size_t)b * Hq + hq) * (size_t)Tq * D * C::ESZ;
+  const uint8_t* Kp = K + ((size_t)b * Hkv + hk) * (size_t)Tk * D * C::ESZ;
+  const uint8_t* Vp = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D * C::ESZ;
   u16* Op = O + ((size_t)b * Hq + hq) * (size_t)Tq * D;
 
   // keys the workgroup needs: [0, kend) = ntiles_all tiles; key group g
@@ -195,50 +216,83 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   if (wrow0 < Lq) kmax = CAUSAL ? min(Lk - 1, min(wrow0 + 31, Lq - 1) + off) : Lk - 1;
   const int kfull = CAUSAL ? min(Lk - 1, wrow0 + off) : Lk - 1;
 
-  // Q fragments (B operand of S^T = K Q^T): row qrow, columns 16 ks + 8 h .. +7
-  bf16x8 qf[C::KS];
+  // Q fragments (B operand of S^T = K Q^T), row qrow.  bf16: columns
+  // 16 ks + 8 h .. +7.  E4M3: bytes 64 kk + 32 h .. +31; the K fragments
+  // use the same bytes of their rows, so every column is paired once.
+  bf16x8 qf[FP8 ? 1 : C::KS];
+  i32x8 qf8[FP8 ? C::KK : 1];
   {
     const bool ok = qrow < Tq;
-    const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? qrow : 0) * D + 8 * h);
-    const uint32_t flip = negq ? 0x80008000u : 0u;
+    if constexpr (FP8) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? qrow : 0) * D + 32 * h);
+      const uint32_t flip = negq ? 0x80808080u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 x = ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
-      x ^= flip;
-      qf[ks] = __builtin_bit_cast(bf16x8, x);
+      for (int kk = 0; kk < C::KK; ++kk) {
+        u32x4 x0 = ok ? src[4 * kk] : u32x4{0u, 0u, 0u, 0u};
+        u32x4 x1 = ok ? src[4 * kk + 1] : u32x4{0u, 0u, 0u, 0u};
+        x0 ^= flip;
+        x1 ^= flip;
+        qf8[kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                        (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+      }
+    } else {
+      const u32x4* src = reinterpret_cast<const u32x4*>(Qp + ((size_t)(ok ? qrow : 0) * D + 8 * h) * 2);
+      const uint32_t flip = negq ? 0x80008000u : 0u;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        u32x4 x = ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+        x ^= flip;
+        qf[ks] = __builtin_bit_cast(bf16x8, x);
+      }
     }
   }
 
   u16* ring = smem + kg * C::RING;
+  uint8_t* ring8 = reinterpret_cast<uint8_t*>(ring);
+  // E4M3: the widened bf16 V tiles follow the stages
+  u16* vwide = ring + C::NS * C::TB;
 
   // HBM -> LDS copy of the group's tile lt (key tile t_begin + lt) into
-  // stage st.  Each 1 KiB wave-load covers 1024/(2D) rows; lane l lands at
-  // byte 16 l of it, i.e. at (row, slot), and fetches the chunk that the
-  // swizzle stores in that slot.  Rows at or past Lk are replaced by row
-  // Lk-1 (finite data; those keys are masked).
+  // stage st.  The tile's 2 LOADS wave-loads (K, then V) are dealt out to
+  // the group's waves.  Each 1 KiB wave-load covers 1024 / (D ESZ) rows;
+  // lane l lands at byte 16 l of it, i.e. at (row, slot), and fetches the
+  // chunk that the swizzle stores in that slot (the E4M3 V tile is stored
+  // as is: it is only read back row by row for widening).  Rows at or past
+  // Lk are replaced by row Lk-1 (finite data; those keys are masked).
   auto issue = [&](int lt, int st) {
     const int kbase = (t_begin + lt) * C::BN;
+    constexpr int CPR = D * C::ESZ / 16;   // 16-byte chunks per row
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const u16* src = t ? Vp : Kp;
-#pragma unroll
-      for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-        const int li = (wg + NWG * i) % C::LOADS;
-        const int e = li * 512 + lane * 8;
-        const int r = e / D, slot = (e % D) / 8;
-        const int ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
-        const int key = min(kbase + r, Lk - 1);
-        const u16* g = src + (size_t)key * D + ch * 8;
-        __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)&ring[(st * 2 + t) * C::TILE + li * 512], 16, 0, 0);
-      }
+    for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
+      const int ci = (wg + NWG * i) % (2 * C::LOADS);
+      const int t = ci / C::LOADS, li = ci - t * C::LOADS;
+      const int p = li * 64 + lane;
+      const int r = p / CPR, slot = p % CPR;
+      int ch;
+      if constexpr (FP8)
+        ch = t ? slot : slot ^ swz_k8<D>(r);
+      else
+        ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
+      const int key = min(kbase + r, Lk - 1);
+      const uint8_t* g = (t ? Vp : Kp) + (size_t)key * D * C::ESZ + ch * 16;
+      __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)(ring8 + (st * 2 + t) * C::TB + li * 1024), 16, 0, 0);
     }
   };
 
-  // per-lane LDS offsets (elements) of the fragments
-  //  K (A of S^T): row 32 kb + r32, logical chunk 2 ks + h
-  int koff[C::KS];
+  // per-lane LDS offsets of the fragments
+  //  K (A of S^T): row 32 kb + r32.  bf16 (elements): logical chunk
+  //  2 ks + h.  E4M3 (bytes): logical chunks 4 kk + 2 h and 4 kk + 2 h + 1.
+  int koff[FP8 ? 1 : C::KS];
+  int koff8[FP8 ? C::KK : 1][2];
+  if constexpr (FP8) {
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) koff[ks] = r32 * D + 8 * ((2 * ks + h) ^ swz_k<D>(r32));
+    for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) koff8[kk][e] = r32 * D + 16 * ((4 * kk + 2 * h + e) ^ swz_k8<D>(r32));
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) koff[ks] = r32 * D + 8 * ((2 * ks + h) ^ swz_k<D>(r32));
+  }
   //  V^T (A of O^T): transposing reads; 16-lane group g covers rows
   //  vr..vr+3 (+16 sh + 32 kb, +8 for the upper half) and logical columns
   //  32 db + 16 (g & 1) + 0..15
@@ -260,9 +314,28 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 
   // ---- S^T = K Q^T for the tile in stage st
   auto do_scores = [&](int st) {
-    lds_u16* Ks = (lds_u16*)&ring[(st * 2 + 0) * C::TILE];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+    if constexpr (FP8) {
+      // v_mfma_f32_32x32x64_f8f6f4 on E4M3 A and B (format 0 for both), no
+      // block scale: exact products of the codes, fp32 sums
+      lds_u8* Ks8 = (lds_u8*)(ring8 + (st * 2 + 0) * C::TB);
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) {
+        lds_u8* k0 = lds_base(Ks8 + koff8[kk][0]);
+        lds_u8* k1 = lds_base(Ks8 + koff8[kk][1]);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const u32x4 x0 = *(const __attribute__((address_space(3))) u32x4*)(k0 + 32 * kb * D);
+          const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(k1 + 32 * kb * D);
+          const i32x8 a = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
+                                (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[kk], s[kb], 0, 0, 0, 0, 0, 0);
+        }
+      }
+      return;
+    }
+    lds_u16* Ks = (lds_u16*)&ring[(st * 2 + 0) * C::TILE];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       // one per-lane base per k-step; the key-block offset folds into the
@@ -326,9 +399,27 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     lsum = ls;
   };
 
-  // ---- O^T += V^T P^T with the V tile in stage st
-  auto do_pv = [&](int st) {
-    lds_u16* Vs = (lds_u16*)&ring[(st * 2 + 1) * C::TILE];
+  // ---- E4M3: widen the V tile of stage stv into bf16 buffer vw (the layout
+  // of a bf16 V stage).  Each thread of the key group takes WE consecutive
+  // elements of one row.
+  auto widen = [&](int stv, int vw) {
+    const int e0 = (wg * 64 + lane) * C::WE;
+    const int r = e0 / D, c0 = e0 % D;
+    lds_u8* src = (lds_u8*)(ring8 + (stv * 2 + 1) * C::TB) + r * D + c0;
+    u16* dst = vwide + vw * C::TILE + r * D;
+    if constexpr (C::WE == 16) {
+      const u32x4 x = *(const __attribute__((address_space(3))) u32x4*)src;
+      *reinterpret_cast<bf16x8*>(dst + 8 * ((c0 / 8) ^ swz_v<D>(r))) = e4m3x8_to_bf16(u32x2{x[0], x[1]});
+      *reinterpret_cast<bf16x8*>(dst + 8 * ((c0 / 8 + 1) ^ swz_v<D>(r))) = e4m3x8_to_bf16(u32x2{x[2], x[3]});
+    } else {
+      const u32x2 x = *(const __attribute__((address_space(3))) u32x2*)src;
+      *reinterpret_cast<bf16x8*>(dst + 8 * ((c0 / 8) ^ swz_v<D>(r))) = e4m3x8_to_bf16(x);
+    }
+  };
+
+  // ---- O^T += V^T P^T with the bf16 V tile at vbase
+  auto do_pv = [&](u16* vbase) {
+    lds_u16* Vs = (lds_u16*)vbase;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       lds_u16* vrow = lds_base(Vs + voff[db]);
@@ -351,19 +442,39 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 #pragma unroll
   for (int p = 0; p < C::NS - 1; ++p)
     if (p < ntiles) issue(p, p);
+  if constexpr (FP8) {
+    // widen tile 0 once every wave's copies of it have landed
+    if (ntiles > 0) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1);
+    __builtin_amdgcn_s_barrier();
+    if (ntiles > 0) widen(0, 0);
+  }
   for (int lt = 0; lt < per; ++lt) {
     const int st = lt % C::NS;
-    // this wave's copies of tile lt have landed and its LDS reads of tile
-    // lt-1 are done; after the barrier the same holds for every wave, so
-    // stage (lt-1) % NS can be refilled with tile lt+NS-1
-    if (lt < ntiles) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - lt);
+    // bf16: this wave's copies of tile lt have landed and its LDS reads of
+    // tile lt-1 are done; after the barrier the same holds for every wave,
+    // so stage (lt-1) % NS can be refilled with tile lt+NS-1.  E4M3: the
+    // same one tile ahead (tile lt+1 is widened in this iteration; tile lt
+    // was widened in the previous one, its writes done before the barrier).
+    if constexpr (FP8) {
+      if (lt + 1 < ntiles)
+        wait_tile<C::VMEM_PER_TILE, C::NS - 3>(ntiles - 2 - lt);
+      else
+        wait_lds();
+    } else {
+      if (lt < ntiles) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - lt);
+    }
     __builtin_amdgcn_s_barrier();
     if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
+    if constexpr (FP8)
+      if (lt + 1 < ntiles) widen((lt + 1) % C::NS, (lt + 1) & 1);
     const int kbase = (t_begin + lt) * C::BN;
     if (lt >= ntiles || kbase > kmax) continue;   // wave-uniform: nothing of this tile for the wave
     do_scores(st);
     do_softmax(kbase);
-    do_pv(st);
+    if constexpr (FP8)
+      do_pv(vwide + (lt & 1) * C::TILE);
+    else
+      do_pv(ring + (st * 2 + 1) * C::TILE);
   }
 
   // ---- merge of the key groups' partials into group 0: with the combined
@@ -432,7 +543,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // ---- epilogue: O = acc / l, LSE = ln(2) (m + log2 l); empty rows -> 0, -inf
   const float ltot = xhalf_sum(lsum);
   const bool has = (qrow < Lq) && (ltot > 0.f);
-  const float inv = has ? 1.f / ltot : 0.f;
+  const float inv = has ? oscale / ltot : 0.f;
   if (qrow < Tq) {
     u16* orow = Op + (size_t)qrow * D;
 #pragma unroll
@@ -450,43 +561,49 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   }
 }
 
-template <int D, int NWG, int KSPLIT, bool CAUSAL>
+template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
 hipError_t launch(const FwdArgs& a, hipStream_t st) {
-  using C = FwdCfg<D, NWG, KSPLIT>;
+  using C = FwdCfg<D, NWG, KSPLIT, FP8>;
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const long long grid = (long long)nqt * a.B * a.Hq;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // c must be > 0 so that exp2(-inf * c) = 0 for masked keys.  For scale = 0
-  // the floor 1e-30 is exact in fp32: every |s| * 1e-30 rounds away against
-  // the row maximum, so all allowed keys get weight exactly 1.
-  const float c = fmaxf(fabsf(a.scale) * 1.4426950408889634f, 1e-30f);
-  const int negq = a.scale < 0.f ? 1 : 0;
+  // scores are scale * (q_scale q).(k_scale k) for E4M3 inputs.  c must be
+  // > 0 so that exp2(-inf * c) = 0 for masked keys.  For a zero factor the
+  // floor 1e-30 is exact in fp32: every |s| * 1e-30 rounds away against the
+  // row maximum, so all allowed keys get weight exactly 1.
+  const double qk = FP8 ? (double)a.scale * a.q_scale * a.k_scale : (double)a.scale;
+  const float c = fmaxf((float)(fabs(qk) * 1.4426950408889634), 1e-30f);
+  const int negq = qk < 0.0 ? 1 : 0;
   // at D=64 both shapes fit two workgroups per CU (64 KiB of LDS, at most
   // 128 registers per lane), so a grid of at most two per CU is resident at
   // once; at D=128 one per CU is, and heavy-first order is kept
   const int zig = (CAUSAL && FWD_ZIGZAG && D == 64 && grid <= 2LL * device_cu_count()) ? 1 : 0;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL>), dim3((unsigned)grid), dim3(C::NT), 0, st,
-                     (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (u16*)a.o, a.lse, a.kv_lens,
-                     a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL, FP8>), dim3((unsigned)grid), dim3(C::NT), 0, st, a.q,
+                     a.k, a.v, (u16*)a.o, a.lse, a.kv_lens, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig,
+                     FP8 ? a.v_scale : 1.f);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool FP8>
 hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
   // 256-row workgroups with one key group fill the chip once there are two
   // per CU; smaller problems take 128-row workgroups whose two key groups
   // split the key range, which halves the longest chain of tiles and
   // doubles the number of workgroups.
   const long long wg256 = (long long)((a.Tq + 255) / 256) * a.B * a.Hq;
-  if (wg256 >= FWD_SPLIT_BELOW) return launch<D, 8, 1, CAUSAL>(a, st);
-  return launch<D, 4, 2, CAUSAL>(a, st);
+  if (wg256 >= FWD_SPLIT_BELOW) return launch<D, 8, 1, CAUSAL, FP8>(a, st);
+  return launch<D, 4, 2, CAUSAL, FP8>(a, st);
+}
+
+template <bool FP8>
+hipError_t launch_all(const FwdArgs& a, hipStream_t st) {
+  if (a.D == 64) return a.causal ? launch_d<64, true, FP8>(a, st) : launch_d<64, false, FP8>(a, st);
+  return a.causal ? launch_d<128, true, FP8>(a, st) : launch_d<128, false, FP8>(a, st);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
-  if (a.D == 64) return a.causal ? launch_d<64, true>(a, st) : launch_d<64, false>(a, st);
-  return a.causal ? launch_d<128, true>(a, st) : launch_d<128, false>(a, st);
-}
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) { return launch_all<false>(a, st); }
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t st) { return launch_all<true>(a, st); }
 
 }  // namespace miattn

@@ -18,6 +18,9 @@ struct FwdArgs {
   int B, Hq, Hkv, Tq, Tk, D;
   float scale;
   int causal;
+  // E4M3 inputs (launch_fwd_fp8): q, k, v hold codes standing for codes
+  // times these scales; o stays bf16
+  float q_scale = 1.f, k_scale = 1.f, v_scale = 1.f;
 };
 
 struct DecodeArgs {
@@ -81,6 +84,7 @@ inline size_t decode_ws_floats(int B, int Hq, int S_max, int D) {
 int device_cu_count();
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);

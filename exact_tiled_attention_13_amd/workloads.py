@@ -23,6 +23,8 @@ decode     KV-cache decode with GQA, B=64, Hq=32, Hkv=8, D=128, one query per
 long       long-context causal prefill, B=1, H=32, T=32768, D=128, bf16.
 decode-fp8 the decode workload with q and the caches as E4M3 codes (FP8, one
            scale per tensor).
+causal-fp8, long-fp8
+           the causal and long prefill workloads with E4M3 Q, K, V.
 =========  ===================================================================
 
 bf16 tensors are drawn as float32 N(0,1) from a seeded ``torch.Generator``
@@ -76,6 +78,10 @@ WORKLOADS = {
                        "decode GQA B=64 Hq=32 Hkv=8 D=128, lengths U[1024,32768]"),
     "long": Workload("long", "fwd", 1, 32, 32, 32768, 32768, 128, "bf16", True, None,
                      "long causal prefill B=1 H=32 T=32768 D=128 bf16"),
+    "causal-fp8": Workload("causal-fp8", "fwd", 4, 16, 16, 1024, 1024, 64, "e4m3", True, None,
+                           "causal prefill B=4 H=16 T=1024 D=64, E4M3 Q/K/V"),
+    "long-fp8": Workload("long-fp8", "fwd", 1, 32, 32, 32768, 32768, 128, "e4m3", True, None,
+                         "long causal prefill B=1 H=32 T=32768 D=128, E4M3 Q/K/V"),
     "decode-fp8": Workload("decode-fp8", "decode", 64, 32, 8, 1, 32768, 128, "e4m3", True, (1024, 32768, False),
                            "decode GQA B=64 Hq=32 Hkv=8 D=128, lengths U[1024,32768], E4M3 q/K/V"),
 }
@@ -155,6 +161,17 @@ def make_decode_inputs(B, Hq, Hkv, S_max, D, lens, seed=0, device="cpu", poison=
     return q, k, v
 
 
+def make_fwd_inputs_fp8(B, Hq, Hkv, Tq, Tk, D, seed=0, device="cpu",
+                        scales=(E4M3_SCALE, E4M3_SCALE, E4M3_SCALE)):
+    """E4M3 Q, K, V for a prefill call (drawn in that order) and their scales."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    qs, ks, vs = scales
+    q = randn_e4m3((B, Hq, Tq, D), g, qs, device)
+    k = randn_e4m3((B, Hkv, Tk, D), g, ks, device)
+    v = randn_e4m3((B, Hkv, Tk, D), g, vs, device)
+    return q, k, v, (qs, ks, vs)
+
+
 def make_decode_inputs_fp8(B, Hq, Hkv, S_max, D, lens, seed=0, device="cpu", poison=False,
                            scales=(E4M3_SCALE, E4M3_SCALE, E4M3_SCALE)):
     """E4M3 q (B, Hq, D) and caches (B, Hkv, S_max, D) plus their scales
@@ -192,6 +209,11 @@ def make(name: str, seed: int = 0, device="cpu", poison=False):
         q, k, v, fp8_scales = make_decode_inputs_fp8(w.B, w.Hq, w.Hkv, w.Tk, w.D, lens, seed, device, poison)
     elif w.kind == "decode":
         q, k, v = make_decode_inputs(w.B, w.Hq, w.Hkv, w.Tk, w.D, lens, seed, device, poison)
+    elif w.dtype == "e4m3":
+        q, k, v, fp8_scales = make_fwd_inputs_fp8(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.D, seed, device)
+        if poison and lens is not None:
+            poison_tail_(k.view(torch.uint8), lens, 0x7F)
+            poison_tail_(v.view(torch.uint8), lens, 0x7F)
     else:
         q, k, v = make_fwd_inputs(w.B, w.Hq, w.Hkv, w.Tq, w.Tk, w.D, w.dtype, seed, device)
         if poison and lens is not None:

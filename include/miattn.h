@@ -84,6 +84,28 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
              const int32_t* kv_lens, int dtype, void* stream);
 
+/*
+ * Prefill attention on 8-bit floating-point (E4M3) inputs: the FP8 inputs
+ * that the self-attention interview question ("Self-Attention:
+ * Implementation, Complexity ..."), Follow-up questions, lists among
+ * FlashAttention-3's additions.  q, k, v hold one E4M3 code per element
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * 0x7f/0xff NaN, largest magnitude 448) in attn_fwd's layouts, each tensor
+ * standing for its codes times its per-tensor scale, so the operation is
+ * attn_fwd's with
+ *   scores = scale * (q_scale q) . (k_scale k) + mask,   O = P (v_scale V).
+ * o is bfloat16 [B, Hq, Tq, D]; lse as attn_fwd (natural log, of those
+ * scores).  The scores are exact products of the codes summed in fp32; V is
+ * widened to bf16 exactly and P rounded to bf16, as in the bf16 path.  Masks,
+ * kv_lens, padding rows and errors as attn_fwd; q_scale, k_scale, v_scale
+ * must be finite and scale * q_scale * k_scale finite in float32 (else
+ * MIATTN_ERR_SHAPE).  Rows at or past a sequence's length may hold any code.
+ */
+int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale,
+                 float q_scale, float k_scale, float v_scale, int causal,
+                 const int32_t* kv_lens, void* stream);
+
 /* Bytes of device workspace the decode calls need for these sizes (split
  * partials plus a little bookkeeping; not used by the float32 path). */
 size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int D);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert ea.attn_abi_version() == 3
+    assert ea.attn_abi_version() == 4
 
 
 def test_strerror_covers_codes(lib):
@@ -72,6 +72,20 @@ def test_fwd_validation(lib, args, code):
         ea.attn_fwd(**a)
     assert e.value.code == code
 
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(v=0), -1), (dict(o=0), -1),
+    (dict(B=0), -2), (dict(Tq=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(scale=float("nan")), -2),
+    (dict(q_scale=float("nan")), -2), (dict(v_scale=float("inf")), -2),
+    (dict(scale=1e30, q_scale=1e10, k_scale=1e10), -2),
+    (dict(D=96), -3), (dict(causal=2), -3),
+])
+def test_fwd_fp8_validation(lib, args, code):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=0, B=1, Hq=2, Hkv=1, Tq=8, Tk=8, D=64, scale=0.125,
+             q_scale=0.01, k_scale=0.02, v_scale=0.03, causal=0, kv_lens=0, stream=0)
+    a.update(args)
+    assert ea.attn_fwd_fp8(**a, check=False) == code
 
 @pytest.mark.parametrize("args,code", [
     (dict(kv_lens=0), -1), (dict(q=0), -1), (dict(k_cache=0), -1),

@@ -1,9 +1,9 @@
-"""GPU parity of the E4M3 (FP8) decode entry points (attn_decode_fp8,
+"""GPU parity of the E4M3 (FP8) entry points (attn_fwd_fp8, attn_decode_fp8,
 attn_decode_paged_fp8 through the C ABI) against the float64 oracle on the
 same codes and scales.
 
 Tolerance: O <= 2e-2 x (size of the V values, ~1 for the default scales),
-LSE <= 1e-3.  The kernel's scores are exact products of the codes summed in
+LSE <= 1e-3.  The kernels' scores are exact products of the codes summed in
 fp32 and V is widened to bf16 exactly, so the rounding left is the bf16 path's
 (P and O rounded to bf16), hence the bf16 bound.  Rows past each length hold
 the NaN code 0x7f and must never reach the result.
@@ -127,3 +127,99 @@ def test_fp8_paged_decode(P, D):
     check(o, lse, o_ref, l_ref, f"fp8 paged P{P} D{D}")
     # same tiles in the same order as the contiguous call: bit-identical
     assert torch.equal(o, o_c) and torch.equal(lse, lse_c)
+
+
+# ------------------------------------------------------------------ prefill
+def run_fwd(B, Hq, Hkv, Tq, Tk, D, causal, lens=None, scale=None, scales=(S0, S0, S0), seed=0, poison=False):
+    q, k, v, sc = workloads.make_fwd_inputs_fp8(B, Hq, Hkv, Tq, Tk, D, seed=seed, scales=scales)
+    if poison and lens is not None:
+        workloads.poison_tail_(k.view(torch.uint8), lens, 0x7F)
+        workloads.poison_tail_(v.view(torch.uint8), lens, 0x7F)
+    scale = 1 / np.sqrt(D) if scale is None else scale
+    kv = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = ea.fwd_fp8(q.cuda(), k.cuda(), v.cuda(), q_scale=sc[0], k_scale=sc[1], v_scale=sc[2], causal=causal,
+                        kv_lens=kv, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_fp8(q, k, v, *sc, scale, causal=causal, kv_lens=lens)
+    return o, lse, o_ref, l_ref
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [1, 63, 200, 513])
+def test_fp8_prefill_small(D, causal, T):
+    """Small grids: the launcher takes the 128-row workgroups with two key groups."""
+    o, lse, o_ref, l_ref = run_fwd(2, 4, 2, T, T, D, causal, seed=T + D)
+    check(o, lse, o_ref, l_ref, f"fp8 prefill T{T} D{D} causal{causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_prefill_large_grid(D, causal):
+    """512+ workgroups of 256 rows: the one-key-group shape."""
+    o, lse, o_ref, l_ref = run_fwd(4, 64, 16, 520, 520, D, causal, seed=7 + D)
+    check(o, lse, o_ref, l_ref, f"fp8 prefill large grid D{D} causal{causal}")
+
+
+@pytest.mark.parametrize("Tq,Tk", [(37, 300), (256, 1000), (1, 777)])
+def test_fp8_prefill_chunked(Tq, Tk):
+    """Tq < Tk: causal aligned bottom-right (a chunk of new queries against a longer cache)."""
+    o, lse, o_ref, l_ref = run_fwd(2, 8, 2, Tq, Tk, 128, True, seed=Tq)
+    check(o, lse, o_ref, l_ref, f"fp8 chunked Tq{Tq} Tk{Tk}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_prefill_padding(causal):
+    lens = [1, 0, 300, 512, 77]
+    o, lse, o_ref, l_ref = run_fwd(5, 4, 4, 512, 512, 64, causal, lens=lens, seed=3, poison=True)
+    check(o, lse, o_ref, l_ref, f"fp8 padding causal{causal}")
+
+
+@pytest.mark.parametrize("scales", [(0.01, 0.02, 0.03), (0.02, -0.015, S0), (S0, S0, -2 * S0)])
+def test_fp8_prefill_scales(scales):
+    o, lse, o_ref, l_ref = run_fwd(2, 4, 2, 300, 300, 128, True, scales=scales, seed=9)
+    check(o, lse, o_ref, l_ref, f"fp8 prefill scales {scales}", vmag=abs(scales[2]) / S0)
+
+
+def test_fp8_prefill_full_size_causal():
+    """The E4M3 causal workload at full size against the full oracle."""
+    w = workloads.WORKLOADS["causal-fp8"]
+    inp = workloads.make("causal-fp8", seed=0)
+    sc = inp["fp8_scales"]
+    o, lse = ea.fwd_fp8(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), q_scale=sc[0], k_scale=sc[1],
+                        v_scale=sc[2], causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_fp8(inp["q"], inp["k"], inp["v"], *sc, w.scale, causal=True)
+    check(o, lse, o_ref, l_ref, "fp8 causal full size")
+
+
+def test_fp8_prefill_long_sampled():
+    """The E4M3 long-context workload (T=32768) on sampled rows, first and last included."""
+    w = workloads.WORKLOADS["long-fp8"]
+    inp = workloads.make("long-fp8", seed=0)
+    sc = inp["fp8_scales"]
+    o, lse = ea.fwd_fp8(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), q_scale=sc[0], k_scale=sc[1],
+                        v_scale=sc[2], causal=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    rows = [(0, 0, 0), (0, 31, w.Tq - 1), (0, 5, 255), (0, 6, 256)]
+    rows += [(0, int(h), int(i)) for h, i in zip(rng.integers(0, w.Hq, 12), rng.integers(0, w.Tq, 12))]
+    o_ref, l_ref = oracle.attention_rows_fp8(inp["q"], inp["k"], inp["v"], rows, *sc, w.scale, causal=True)
+    og = torch.stack([o[0, h, i] for _, h, i in rows])
+    lg = torch.stack([lse[0, h, i] for _, h, i in rows])
+    check(og, lg, o_ref, l_ref, "fp8 long sampled rows")
+
+
+def test_fp8_prefill_matches_bf16_path_on_exact_values():
+    """E4M3 values are exact in bf16: with unit scales the E4M3 prefill and the
+    bf16 prefill see the same numbers; both stay within the bf16 bound of the
+    oracle and of each other."""
+    q, k, v, _ = workloads.make_fwd_inputs_fp8(2, 8, 4, 700, 700, 128, seed=21, scales=(1.0, 1.0, 1.0))
+    # N(0,1) codes at unit scale: values up to ~4 with 3-bit mantissas
+    o8, l8 = ea.fwd_fp8(q.cuda(), k.cuda(), v.cuda(), q_scale=1.0, k_scale=1.0, v_scale=1.0, causal=True,
+                        scale=0.05)
+    ob, lb = ea.fwd(q.to(torch.bfloat16).cuda(), k.to(torch.bfloat16).cuda(), v.to(torch.bfloat16).cuda(),
+                    causal=True, scale=0.05)
+    torch.cuda.synchronize()
+    assert float((o8.float() - ob.float()).abs().max()) <= 2e-2
+    assert float((l8 - lb).abs().max()) <= 1e-3
