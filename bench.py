@@ -11,7 +11,8 @@ workload (B=4, H=16, T=1024, D=64, bf16) in TFLOP/s of algorithmic work
 KV-cache decode step of the GQA decode workload (B=64, Hq=32, Hkv=8, D=128,
 lengths 1024..32768) in GB/s of algorithmic bytes (the K/V rows each sequence
 needs plus q, o, lse and lengths), reported under "decode", the same step on
-E4M3 (FP8) q and caches under "decode_fp8", and the gradients
+E4M3 (FP8) q and caches under "decode_fp8", the causal prefill on E4M3 Q, K,
+V under "prefill_fp8", and the gradients
 of the causal workload (10*D flops per unmasked pair: the five products of
 the backward), reported under "backward".  Steps are
 replayed from a HIP graph (a fixed number of calls per graph) so that host
@@ -43,13 +44,17 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
 # kernel name (as rocprofv3 reports it, substring) -> sources it is built from
 KERNEL_SOURCES = {
-    "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h"],
+    "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h", "launch.h"],
     "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
     "decode_split_kernel": ["decode.hip", "device_common.h", "launch.h"],
 }
 COPY_BYTES = 1 << 30          # size of the calibration copy
 
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU * 2.4 GHz * 4096 dense bf16 flop/clk/CU
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU * 2.4 GHz * 8192 dense fp8 flop/clk/CU
+# The E4M3 prefill runs Q K^T (half the flops) on fp8 and P V on bf16, so its
+# matrix peak is the harmonic combination of the two.
+PEAK_FP8_BF16_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 CALLS_PER_GRAPH = 20
@@ -132,19 +137,29 @@ def setup_prefill(torch, name):
     W = w["workload"]
     q, k, v = (w[x].cuda() for x in ("q", "k", "v"))
     kv = None if w["kv_lens"] is None else w["kv_lens"].cuda()
-    o = torch.empty_like(q)
     lse = torch.empty((W.B, W.Hq, W.Tq), dtype=torch.float32, device="cuda")
-    dt = ea.MIATTN_BF16 if W.dtype == "bf16" else ea.MIATTN_F32
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq, W.Hkv, W.Tq, W.Tk,
-            W.D, W.scale, int(W.causal), 0 if kv is None else kv.data_ptr(), dt)
+    kvp = 0 if kv is None else kv.data_ptr()
+    if W.dtype == "e4m3":
+        o = torch.empty((W.B, W.Hq, W.Tq, W.D), dtype=torch.bfloat16, device="cuda")
+        qs, ks, vs = w["fp8_scales"]
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq, W.Hkv, W.Tq,
+                W.Tk, W.D, W.scale, qs, ks, vs, int(W.causal), kvp)
 
-    def step():
-        ea.attn_fwd(*args, torch.cuda.current_stream().cuda_stream)
+        def step():
+            ea.attn_fwd_fp8(*args, torch.cuda.current_stream().cuda_stream)
+    else:
+        o = torch.empty_like(q)
+        dt = ea.MIATTN_BF16 if W.dtype == "bf16" else ea.MIATTN_F32
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), W.B, W.Hq, W.Hkv, W.Tq,
+                W.Tk, W.D, W.scale, int(W.causal), kvp, dt)
+
+        def step():
+            ea.attn_fwd(*args, torch.cuda.current_stream().cuda_stream)
 
     pairs = prefill_pairs(W.B, W.Hq, W.Tq, W.Tk, W.causal, w["lens"])
     flops = 4 * W.D * pairs
-    elem = 2 if W.dtype == "bf16" else 4
-    io_bytes = (2 * q.numel() + k.numel() + v.numel()) * elem + lse.numel() * 4
+    elem = {"bf16": 2, "f32": 4, "e4m3": 1}[W.dtype]
+    io_bytes = (q.numel() + k.numel() + v.numel()) * elem + o.numel() * o.element_size() + lse.numel() * 4
     keep = (q, k, v, kv, o, lse)
     return dict(w=w, W=W, step=step, flops=flops, io_bytes=io_bytes, keep=keep, out=(o, lse))
 
@@ -314,8 +329,11 @@ def cpu_baseline_prefill(name, budget_s):
     for b in range(W.B):
         for h in range(W.Hq):
             lens = None if w["lens"] is None else w["lens"][b:b + 1]
-            oracle.attention(q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1], v[b:b + 1, h // G:h // G + 1],
-                             W.scale, W.causal, lens)
+            qh, kh, vh = q[b:b + 1, h:h + 1], k[b:b + 1, h // G:h // G + 1], v[b:b + 1, h // G:h // G + 1]
+            if W.dtype == "e4m3":
+                oracle.attention_fp8(qh, kh, vh, *w["fp8_scales"], W.scale, W.causal, lens)
+            else:
+                oracle.attention(qh, kh, vh, W.scale, W.causal, lens)
             done_flops += 4 * W.D * prefill_pairs(1, 1, W.Tq, W.Tk, W.causal, lens)
             heads += 1
             if time.perf_counter() - t0 > budget_s:
@@ -436,7 +454,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="causal",
-                    choices=["causal", "long", "ragged", "decode", "decode-paged", "decode-fp8", "single"])
+                    choices=["causal", "long", "ragged", "decode", "decode-paged", "decode-fp8", "causal-fp8",
+                             "long-fp8", "single"])
     ap.add_argument("--page-size", type=int, default=16, help="page size of --workload decode-paged")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements of the default run")
     ap.add_argument("--backward", action="store_true",
@@ -521,9 +540,9 @@ def main():
     check_graph_replay(torch, runner, pre["step"], pre["out"])
     ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
     W = pre["W"]
-    kname = "fwd_bf16_kernel" if W.dtype == "bf16" else "fwd_f32_kernel"
+    kname = "fwd_f32_kernel" if W.dtype == "f32" else "fwd_bf16_kernel"
     tflops = pre["flops"] / (ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if W.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    peak = {"bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_MFMA_TFLOPS, "e4m3": PEAK_FP8_BF16_TFLOPS}[W.dtype]
     line = dict(
         metric="prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
         value=round(tflops, 3), unit="TFLOP/s", n_gpus=1, steps=n, warmup=args.warmup,
@@ -568,6 +587,22 @@ def main():
                                                 traffic=traffic_for("decode_split_kernel", "decode-fp8"),
                                                 kernels="decode_split + decode_merge"))
         del dec, drun
+    if args.workload == "causal" and not args.no_decode:
+        # the same causal prefill on E4M3 inputs
+        torch.cuda.empty_cache()
+        pf = setup_prefill(torch, "causal-fp8")
+        prun = Graphed(torch, pf["step"])
+        check_graph_replay(torch, prun, pf["step"], pf["out"])
+        pms, pwall, pn = time_steps(torch, prun, max(20, args.steps // 4), max(5, args.warmup // 4))
+        ptf = pf["flops"] / (pms * 1e-3) / 1e12
+        line["prefill_fp8"] = dict(workload=pf["W"].note, value=round(ptf, 3), unit="TFLOP/s", steps=pn,
+                                   ms_per_step=round(pms, 5), flops_per_step=pf["flops"], dtype="e4m3",
+                                   roofline=dict(bound="mfma", achieved=round(ptf, 3),
+                                                 peak=round(PEAK_FP8_BF16_TFLOPS, 1), unit="TFLOP/s",
+                                                 frac=round(ptf / PEAK_FP8_BF16_TFLOPS, 4), traffic=None,
+                                                 kernel="fwd_bf16_kernel (E4M3 instance)",
+                                                 peak_note="Q K^T on fp8 (5033 TFLOP/s), P V on bf16 (2517)"))
+        del pf, prun
     if args.workload == "causal" and not args.no_backward:
         torch.cuda.empty_cache()
         bw = setup_backward(torch, "causal")
