@@ -487,6 +487,7 @@ def main():
 
     ea.load()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    launch_table = f"{ea.attn_tile_table_size()} tuned entries" if ea.attn_tile_table_size() else "built-in rule"
     torch.cuda.set_device(0)
 
     line = {}
@@ -505,7 +506,8 @@ def main():
                     warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak",
                     vs_baseline=None, dtype="e4m3" if fp8 else "bf16", data="synthetic",
                     config=dict(workload=note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
-                                sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU"),
+                                sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU",
+                                launch_table=launch_table),
                     roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
                                   frac=round(gbs / PEAK_HBM_GBS, 4),
                                   traffic=None if paged else traffic_for("decode_split_kernel", args.workload),
@@ -549,7 +551,7 @@ def main():
         ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype=W.dtype, data="synthetic",
         config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk, D=W.D, causal=W.causal,
-                    flops_per_step=pre["flops"], parallelism="single GPU"),
+                    flops_per_step=pre["flops"], parallelism="single GPU", launch_table=launch_table),
         roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=peak, unit="TFLOP/s",
                       frac=round(tflops / peak, 4), traffic=traffic_for(kname, args.workload), kernel=kname,
                       kernel_ms=round(ms, 5)),

@@ -37,14 +37,18 @@ from ._lib import (  # noqa: F401
     attn_decode_workspace_size,
     attn_fwd,
     attn_fwd_fp8,
+    attn_set_tile_table,
     attn_strerror,
+    attn_tile_choice,
+    attn_tile_table_size,
     load,
 )
 
 __all__ = ["fwd", "fwd_fp8", "decode", "decode_paged", "decode_fp8", "decode_paged_fp8", "bwd", "attn_fwd", "attn_decode",
            "attn_decode_paged", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_fwd_fp8",
            "attn_decode_workspace_size", "attn_bwd",
-           "attn_bwd_workspace_size", "attn_strerror", "MiattnError", "load"]
+           "attn_bwd_workspace_size", "attn_set_tile_table", "attn_tile_table_size", "attn_tile_choice",
+           "attn_strerror", "MiattnError", "load"]
 
 
 def _torch():

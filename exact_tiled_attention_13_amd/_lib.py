@@ -12,9 +12,14 @@ LIB_PATH = os.environ.get("MIATTN_LIB") or os.path.join(_PKG, "libmiattn.so")
 
 MIATTN_F32 = 0
 MIATTN_BF16 = 1
+MIATTN_E4M3 = 2
+MIATTN_TILE_FWD = 0
+MIATTN_TILE_DECODE = 1
+MIATTN_TILE_FIELDS = 8
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_decode_fp8",
-            "attn_decode_paged_fp8", "attn_bwd_workspace_size", "attn_bwd", "attn_strerror", "attn_abi_version")
+            "attn_decode_paged_fp8", "attn_bwd_workspace_size", "attn_bwd", "attn_set_tile_table",
+            "attn_tile_table_size", "attn_tile_choice", "attn_strerror", "attn_abi_version")
 
 _lib = None
 
@@ -56,11 +61,20 @@ def load() -> ctypes.CDLL:
     lib.attn_bwd_workspace_size.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, vp, sz, i, vp]
     lib.attn_bwd.restype = i
+    lib.attn_set_tile_table.argtypes = [vp, i]
+    lib.attn_set_tile_table.restype = i
+    lib.attn_tile_table_size.argtypes = []
+    lib.attn_tile_table_size.restype = i
+    lib.attn_tile_choice.argtypes = [i, i, i, i, ctypes.c_longlong, vp]
+    lib.attn_tile_choice.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
     lib.attn_abi_version.restype = i
     _lib = lib
+    if os.environ.get("MIATTN_TILES", "") != "off":
+        from . import tiles
+        tiles.apply_default(lib)
     return lib
 
 
@@ -147,3 +161,28 @@ def attn_decode_paged_fp8(q, k_pages, v_pages, block_table, o, lse, B, Hq, Hkv, 
                                         float(scale), float(q_scale), float(k_scale), float(v_scale),
                                         kv_lens or None, workspace or None, workspace_bytes, stream or None)
     return _check(code) if check else code
+
+
+def attn_set_tile_table(entries, check=True):
+    """entries: a sequence of MIATTN_TILE_FIELDS-int rows (see include/miattn.h)."""
+    rows = [list(map(int, e)) for e in entries]
+    for r in rows:
+        if len(r) != MIATTN_TILE_FIELDS:
+            raise ValueError(f"a tile-table entry has {MIATTN_TILE_FIELDS} fields, got {len(r)}")
+    arr = (ctypes.c_int32 * (MIATTN_TILE_FIELDS * max(1, len(rows))))(*[x for r in rows for x in r])
+    code = load().attn_set_tile_table(ctypes.cast(arr, ctypes.c_void_p), len(rows))
+    return _check(code) if check else code
+
+
+def attn_tile_table_size() -> int:
+    return int(load().attn_tile_table_size())
+
+
+def attn_tile_choice(op, dtype, D, causal, size, check=True):
+    """(v0, v1) that a launch with this key uses (see include/miattn.h)."""
+    out = (ctypes.c_int32 * 2)()
+    code = load().attn_tile_choice(int(op), int(dtype), int(D), int(causal), int(size), ctypes.cast(out, ctypes.c_void_p))
+    if check:
+        _check(code)
+        return int(out[0]), int(out[1])
+    return code

@@ -45,6 +45,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "../../include/miattn.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -557,9 +558,11 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   const double qk = FP8 ? (double)a.scale * a.q_scale * a.k_scale : (double)a.scale;
   const float c = (float)(fabs(qk) * 1.4426950408889634);
   const int negq = qk < 0.0 ? 1 : 0;
-  // two workgroups (8 waves) per CU, never more waves than work items
+  // workgroups per CU from the launch table (built-in: two, i.e. 8 waves),
+  // never more waves than work items
   const long long items = (long long)a.B * NS * a.Hkv * NHB;
-  const long long wgs = std::min<long long>(2LL * device_cu_count(), (items + kNW - 1) / kNW);
+  const long long per_cu = choose_decode_wgs_per_cu(FP8 ? MIATTN_E4M3 : MIATTN_BF16, D, items);
+  const long long wgs = std::min<long long>(per_cu * device_cu_count(), (items + kNW - 1) / kNW);
   const int nwav = (int)wgs * kNW;
   hipLaunchKernelGGL((decode_split_kernel<D, PAGED, FP8>), dim3((unsigned)wgs), dim3(64 * kNW), 0, st, a.q,
                      a.k_cache, a.v_cache, a.kv_lens, a.ws_o, a.ws_ml, a.ws_idx, a.B, a.Hq, a.Hkv, a.S_max, NS, NHB,

@@ -42,18 +42,10 @@
 // stored unpadded, with the 16-byte chunks of each row XOR-permuted (swz_k,
 // swz_v below) so that the 16-byte K reads and the transposing V reads are
 // free of bank conflicts.
+#include "../../include/miattn.h"
 #include "device_common.h"
 #include "launch.h"
 
-// Workgroup count below which the launcher switches to 128-row workgroups
-// with two key groups (the chip has 256 CUs and holds two 256-row
-// workgroups per CU).
-#ifndef FWD_SPLIT_BELOW
-#define FWD_SPLIT_BELOW 512
-#endif
-#ifndef FWD_ZIGZAG
-#define FWD_ZIGZAG 1
-#endif
 
 namespace miattn {
 namespace {
@@ -562,7 +554,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 }
 
 template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
-hipError_t launch(const FwdArgs& a, hipStream_t st) {
+hipError_t launch(const FwdArgs& a, hipStream_t st, int zig_choice) {
   using C = FwdCfg<D, NWG, KSPLIT, FP8>;
   const int nqt = (a.Tq + C::BM - 1) / C::BM;
   const long long grid = (long long)nqt * a.B * a.Hq;
@@ -574,10 +566,12 @@ hipError_t launch(const FwdArgs& a, hipStream_t st) {
   const double qk = FP8 ? (double)a.scale * a.q_scale * a.k_scale : (double)a.scale;
   const float c = fmaxf((float)(fabs(qk) * 1.4426950408889634), 1e-30f);
   const int negq = qk < 0.0 ? 1 : 0;
-  // at D=64 both shapes fit two workgroups per CU (64 KiB of LDS, at most
-  // 128 registers per lane), so a grid of at most two per CU is resident at
-  // once; at D=128 one per CU is, and heavy-first order is kept
-  const int zig = (CAUSAL && FWD_ZIGZAG && D == 64 && grid <= 2LL * device_cu_count()) ? 1 : 0;
+  // built-in zig-zag rule: at D=64 both shapes fit two workgroups per CU
+  // (64 KiB of LDS, at most 128 registers per lane), so a grid of at most
+  // two per CU is resident at once; at D=128 one per CU is, and
+  // heavy-first order is kept.  The launch table may force it either way.
+  const int zig = zig_choice >= 0 ? zig_choice
+                                  : ((CAUSAL && D == 64 && grid <= 2LL * device_cu_count()) ? 1 : 0);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL, FP8>), dim3((unsigned)grid), dim3(C::NT), 0, st, a.q,
                      a.k, a.v, (u16*)a.o, a.lse, a.kv_lens, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig,
                      FP8 ? a.v_scale : 1.f);
@@ -589,10 +583,12 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
   // 256-row workgroups with one key group fill the chip once there are two
   // per CU; smaller problems take 128-row workgroups whose two key groups
   // split the key range, which halves the longest chain of tiles and
-  // doubles the number of workgroups.
+  // doubles the number of workgroups.  That is the built-in rule; the
+  // launch table may choose otherwise per size bucket.
   const long long wg256 = (long long)((a.Tq + 255) / 256) * a.B * a.Hq;
-  if (wg256 >= FWD_SPLIT_BELOW) return launch<D, 8, 1, CAUSAL, FP8>(a, st);
-  return launch<D, 4, 2, CAUSAL, FP8>(a, st);
+  const FwdChoice ch = choose_fwd(FP8 ? MIATTN_E4M3 : MIATTN_BF16, D, CAUSAL ? 1 : 0, wg256);
+  if (ch.shape == 0) return launch<D, 8, 1, CAUSAL, FP8>(a, st, ch.zig);
+  return launch<D, 4, 2, CAUSAL, FP8>(a, st, ch.zig);
 }
 
 template <bool FP8>

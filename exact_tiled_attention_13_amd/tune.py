@@ -1,0 +1,148 @@
+"""Tuner for the launch-choice table (run on the GPU):
+
+    python -m exact_tiled_attention_13_amd.tune [--out PATH] [--reps N]
+
+For every (operation, dtype, D, causal, size bucket) it times each launch
+choice on a representative synthetic problem of that bucket, with the
+choice forced through a one-entry table, and records the fastest together
+with all timings.  The result is the JSON file ``tiles.py`` loads (by
+default ``tiles_gfx950.json`` next to this file).  Buckets are keyed by the
+size the library computes for the call (include/miattn.h):
+
+* prefill: ceil(Tq / 256) * B * Hq; problems with Tq = Tk = 1024, Hkv = Hq;
+* decode: B * ceil(S_max / 512) * Hkv * ceil(G / 16); problems with B = 64,
+  Hq = 32, Hkv = 8 and every sequence at full length.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import statistics
+import sys
+
+import torch
+
+from . import _lib, tiles
+from . import fwd, fwd_fp8, decode, decode_fp8
+from . import workloads
+
+# (size_lo, size_hi, representative size).  Up to 256 the 128-row shape's
+# grid (2 * size workgroups) is resident at once on 256 CUs, which is where
+# zig-zag pairing can help, so that boundary is a bucket edge.
+FWD_BUCKETS = [(1, 63, 48), (64, 127, 96), (128, 256, 256), (257, 511, 384), (512, 1023, 768),
+               (1024, 2047, 1536), (2048, 2**31 - 1, 3072)]
+DEC_BUCKETS = [(1, 4095, 2048), (4096, 16383, 8192), (16384, 2**31 - 1, 32768)]
+T = 1024
+
+
+def _time(fn, reps, calls):
+    """Median over reps of the mean time (ms) of `calls` back-to-back calls."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(calls):
+            fn()
+        b.record()
+        b.synchronize()
+        out.append(a.elapsed_time(b) / calls)
+    return statistics.median(out)
+
+
+def _forced(row):
+    _lib.attn_set_tile_table([row])
+
+
+def tune_fwd(dtype, D, causal, reps):
+    entries = []
+    for lo, hi, wg in FWD_BUCKETS:
+        BH = wg // math.ceil(T / 256)
+        B = math.gcd(BH, 8)
+        H = BH // B
+        g = torch.Generator(device="cuda").manual_seed(0)
+        if dtype == "e4m3":
+            q, k, v = (workloads.randn_e4m3((B, H, T, D), g, device="cuda") for _ in range(3))
+            s = workloads.E4M3_SCALE
+            call = lambda: fwd_fp8(q, k, v, q_scale=s, k_scale=s, v_scale=s, causal=bool(causal))  # noqa: E731
+        else:
+            q, k, v = (workloads.randn_bf16((B, H, T, D), g, device="cuda") for _ in range(3))
+            call = lambda: fwd(q, k, v, causal=bool(causal))  # noqa: E731
+        size = math.ceil(T / 256) * B * H
+        cands = [(0, z) for z in ((0, 1) if causal else (0,))] + [(1, z) for z in ((0, 1) if causal else (0,))]
+        times = {}
+        for shape, zig in cands:
+            _forced([tiles.OPS["fwd"], tiles.DTYPES[dtype], D, causal, 0, 2**31 - 1, shape, zig])
+            times[f"{shape},{zig}"] = round(_time(call, reps, 10), 5)
+        best = min(times, key=times.get)
+        entries.append(dict(op="fwd", dtype=dtype, D=D, causal=causal, size_lo=lo, size_hi=hi,
+                            choice=[int(x) for x in best.split(",")], times_ms=times,
+                            problem=dict(B=B, Hq=H, Hkv=H, Tq=T, Tk=T, size=size)))
+        print(f"fwd {dtype} D{D} causal{causal} size {size:5d}: {times} -> {best}", flush=True)
+        del q, k, v
+    return entries
+
+
+def tune_decode(dtype, D, reps):
+    entries = []
+    B, Hq, Hkv = 64, 32, 8
+    for lo, hi, S in DEC_BUCKETS:
+        g = torch.Generator(device="cuda").manual_seed(0)
+        lens = torch.full((B,), S, dtype=torch.int32, device="cuda")
+        if dtype == "e4m3":
+            q = workloads.randn_e4m3((B, Hq, D), g, device="cuda")
+            kc = workloads.randn_e4m3((B, Hkv, S, D), g, device="cuda")
+            vc = workloads.randn_e4m3((B, Hkv, S, D), g, device="cuda")
+            s = workloads.E4M3_SCALE
+            call = lambda: decode_fp8(q, kc, vc, lens, q_scale=s, k_scale=s, v_scale=s)  # noqa: E731
+        else:
+            q = workloads.randn_bf16((B, Hq, D), g, device="cuda")
+            kc = workloads.randn_bf16((B, Hkv, S, D), g, device="cuda")
+            vc = workloads.randn_bf16((B, Hkv, S, D), g, device="cuda")
+            call = lambda: decode(q, kc, vc, lens)  # noqa: E731
+        size = B * math.ceil(S / 512) * Hkv * math.ceil(Hq // Hkv / 16)
+        times = {}
+        for per_cu in (1, 2, 3, 4):
+            _forced([tiles.OPS["decode"], tiles.DTYPES[dtype], D, 1, 0, 2**31 - 1, per_cu, 0])
+            times[str(per_cu)] = round(_time(call, reps, 5), 5)
+        best = min(times, key=times.get)
+        entries.append(dict(op="decode", dtype=dtype, D=D, causal=1, size_lo=lo, size_hi=hi,
+                            choice=[int(best), 0], times_ms=times,
+                            problem=dict(B=B, Hq=Hq, Hkv=Hkv, S_max=S, lengths="all S_max", size=size)))
+        print(f"decode {dtype} D{D} size {size:6d}: {times} -> {best}", flush=True)
+        del q, kc, vc
+    return entries
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=tiles.DEFAULT_PATH)
+    ap.add_argument("--reps", type=int, default=5)
+    args = ap.parse_args(argv)
+    if not torch.cuda.is_available():
+        sys.exit("the tuner needs a GPU")
+    _lib.load()
+    entries = []
+    try:
+        for dtype in ("bf16", "e4m3"):
+            for D in (64, 128):
+                for causal in (0, 1):
+                    entries += tune_fwd(dtype, D, causal, args.reps)
+                entries += tune_decode(dtype, D, args.reps)
+    finally:
+        _lib.attn_set_tile_table([])
+    doc = dict(arch="gfx950", device=torch.cuda.get_device_name(0), fields=tiles.FIELDS,
+               note="written by python -m exact_tiled_attention_13_amd.tune; times in ms per call",
+               entries=entries)
+    tiles.entries_from_json(doc)   # the document must load
+    with open(args.out, "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(f"wrote {len(entries)} entries to {args.out}")
+
+
+if __name__ == "__main__":
+    main()

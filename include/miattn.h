@@ -62,7 +62,8 @@ extern "C" {
 
 enum {
   MIATTN_F32 = 0,  /* float32 q/k/v/o */
-  MIATTN_BF16 = 1  /* bfloat16 q/k/v/o */
+  MIATTN_BF16 = 1, /* bfloat16 q/k/v/o */
+  MIATTN_E4M3 = 2  /* E4M3 codes (the *_fp8 calls); used as a launch-table key only */
 };
 
 enum {
@@ -208,6 +209,38 @@ size_t attn_bwd_workspace_size(int B, int Hq, int Tq);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
              const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * Launch-choice table.  The NumPy tiled-attention build guide, section
+ * Extending It, suggests picking the tile configuration per head size and
+ * hardware by measurement and persisting the result; here the compiled
+ * kernels take their launch shape as a runtime choice, looked up in this
+ * table (the Python binding fills it from the JSON file its tuner writes).
+ * Keys not covered, or no table, use the built-in rule.  Every choice gives
+ * a correct result; only speed differs.
+ *
+ * An entry is MIATTN_TILE_FIELDS int32:
+ *   { op, dtype, D, causal, size_lo, size_hi, v0, v1 }
+ *   op    MIATTN_TILE_FWD: attn_fwd (dtype MIATTN_BF16) and attn_fwd_fp8
+ *         (MIATTN_E4M3); size = ceil(Tq / 256) * B * Hq; v0 = 0 for
+ *         256-row workgroups with one key group, 1 for 128-row workgroups
+ *         whose two key groups split the keys; v1 = 1 to pair causal query
+ *         tiles long with short, 0 not to, -1 for the built-in rule.
+ *   op    MIATTN_TILE_DECODE: the bf16 and E4M3 decode calls, causal = 1;
+ *         size = B * ceil(S_max / 512) * Hkv * ceil(Hq / Hkv / 16);
+ *         v0 = workgroups of the split kernel per compute unit (1..8),
+ *         v1 = 0.
+ * The first entry whose key matches (size_lo <= size <= size_hi) wins.
+ * attn_set_tile_table copies n entries (n <= 256; n = 0 clears the table)
+ * and returns MIATTN_ERR_UNSUPPORTED for an invalid entry, leaving the old
+ * table in place.  It is thread-safe; calls running concurrently see the
+ * old or the new table.  attn_tile_choice writes the (v0, v1) a launch with
+ * that key would use (v1 = -1: the built-in zig-zag rule).
+ */
+enum { MIATTN_TILE_FWD = 0, MIATTN_TILE_DECODE = 1, MIATTN_TILE_FIELDS = 8 };
+int attn_set_tile_table(const int32_t* entries, int n);
+int attn_tile_table_size(void);
+int attn_tile_choice(int op, int dtype, int D, int causal, long long size, int32_t* out);
 
 /* Static text for a return code; for MIATTN_ERR_HIP, the last HIP error seen
  * by the calling thread. */
