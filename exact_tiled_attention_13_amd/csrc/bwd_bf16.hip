@@ -30,6 +30,8 @@
 // XOR-ed by swz(r), chosen so that both read patterns on the same tile are
 // free of bank conflicts: 16-byte reads of 16 consecutive rows (one chunk
 // each) and transposing 8-byte reads of 4 rows x 4 chunks per 32 lanes.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -312,10 +314,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ---------------------------------------------------------------- bwd_dkdv
-// (two waves per SIMD at D=64; at D=128 the K, V fragments and the dK, dV
-// accumulators alone take 192 registers per lane, so one)
+// At D=128 one pass would hold the K and V fragments and the dK and dV
+// accumulators (192 registers per lane) plus the step's scores and
+// addresses: past 256 VGPRs, where the compiler parks the accumulators in
+// AccVGPRs and copies all 128 of them both ways on every step.  So D=128
+// runs two passes over the query tiles: first S, P and dV, then S, dP, dS
+// and dK (S is computed twice, 25% more matrix work), each pass holding 64
+// accumulators, which fits two waves per SIMD.  D=64 runs both in one pass.
 template <int D, int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1, D == 64 ? 2 : 1))) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
@@ -325,6 +332,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
   constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW;
   constexpr int VM_PER_STEP = 2 * PER + 2;   // Q, dO tiles + Lc, Drow rows
   constexpr int STAGE = 2 * TILE + 2 * 64 * 2;   // u16 elements: Q, dO, then 64 Lc + 64 Drow floats
+  constexpr bool SPLIT = D == 128;
   __shared__ __attribute__((aligned(1024))) u16 smem[NS * STAGE];
 
   const int tid = threadIdx.x;
@@ -356,19 +364,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
   const int nsteps = G * nsteps_h;
   const int qwave_first = CAUSAL ? wkey0 - off : 0;   // first row that sees this wave's first key
 
-  // K and V fragments of this lane's key (B operands of S = Q K^T, dP = dO V^T)
-  bf16x8 kf[KS], vf[KS];
+  // K fragments of this lane's key (B operand of S = Q K^T)
+  bf16x8 kf[KS];
   const bool kok = key < Lk;
   row_fragments<KS>(kf, Kp, key, kok, h, negk ? 0x80008000u : 0u);
-  row_fragments<KS>(vf, Vp, key, kok, h, 0u);
-
   const TileOffsets<D> to(lane);
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) {
-    dk[i] = f32x16{};
-    dv[i] = f32x16{};
-  }
+  const size_t krow = ((size_t)b * Hkv + hk) * (size_t)Tk + key;
 
   auto step_rows = [&](int sidx, int& hq, int& q0) {
     const int g = sidx / nsteps_h;
@@ -389,91 +390,126 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D == 64
     __builtin_amdgcn_global_load_lds((gptr_t*)(Drow + qbase + row), (lptr_t*)(base + 2 * TILE + 128), 4, 0, 0);
   };
 
+  // One pass over the query tiles.  PASS 0: dV only; 1: dK only; 2: both.
+  auto run = [&](auto PASSC) {
+    constexpr int PASS = decltype(PASSC)::value;
+    constexpr bool DO_V = PASS != 1, DO_K = PASS != 0;
+    // V fragments of this lane's key (B operand of dP = dO V^T)
+    bf16x8 vf[DO_K ? KS : 1];
+    if constexpr (DO_K) row_fragments<KS>(vf, Vp, key, kok, h, 0u);
+    f32x16 dk[DO_K ? DB : 1], dv[DO_V ? DB : 1];
 #pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nsteps) issue(p, p);
-  for (int sidx = 0; sidx < nsteps; ++sidx) {
-    const int st = sidx % NS;
-    wait_tile<VM_PER_STEP, NS - 2>(nsteps - 1 - sidx);
-    __builtin_amdgcn_s_barrier();
-    if (sidx + NS - 1 < nsteps) issue(sidx + NS - 1, (sidx + NS - 1) % NS);
-    int hq, q0;
-    step_rows(sidx, hq, q0);
-    // wave-uniform: no row of this step sees a key of this wave
-    if (wkey0 >= Lk || q0 + BMQ - 1 < qwave_first) continue;
-    lds_u16* Qs = (lds_u16*)&smem[st * STAGE];
-    lds_u16* Gs = Qs + TILE;
-    lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
-    lds_f32* Ds = Ls + 64;
-    // S = Q K^T and dP = dO V^T (32 queries x 32 keys; a lane owns a key)
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 qa = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Qs + to.row[ks]));
-      const bf16x8 ga = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Gs + to.row[ks]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+    for (int i = 0; i < DB; ++i) {
+      if constexpr (DO_K) dk[i] = f32x16{};
+      if constexpr (DO_V) dv[i] = f32x16{};
     }
-    // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
-    const bool need_mask = (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
-    if (need_mask) {
+
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool ok = i < Lq && key < Lk && (!CAUSAL || key <= i + off);
-        s[r] = ok ? s[r] : kNegInf;
-        dp[r] = ok ? dp[r] : 0.f;
+    for (int p = 0; p < NS - 1; ++p)
+      if (p < nsteps) issue(p, p);
+    for (int sidx = 0; sidx < nsteps; ++sidx) {
+      const int st = sidx % NS;
+      wait_tile<VM_PER_STEP, NS - 2>(nsteps - 1 - sidx);
+      __builtin_amdgcn_s_barrier();
+      if (sidx + NS - 1 < nsteps) issue(sidx + NS - 1, (sidx + NS - 1) % NS);
+      int hq, q0;
+      step_rows(sidx, hq, q0);
+      // wave-uniform: no row of this step sees a key of this wave
+      if (wkey0 >= Lk || q0 + BMQ - 1 < qwave_first) continue;
+      lds_u16* Qs = (lds_u16*)&smem[st * STAGE];
+      lds_u16* Gs = Qs + TILE;
+      lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
+      lds_f32* Ds = Ls + 64;
+      // S = Q K^T (and dP = dO V^T) (32 queries x 32 keys; a lane owns a key)
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 qa = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Qs + to.row[ks]));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        if constexpr (DO_K) {
+          const bf16x8 ga = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Gs + to.row[ks]));
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+        }
       }
-    }
-    bf16x8 pf[2], dsf[2];
+      // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
+      const bool need_mask = (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
+      if (need_mask) {
 #pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-      const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 4 * h);
-      const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 8 + 4 * h);
-      const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 4 * h);
-      const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 8 + 4 * h);
-      uint32_t pp[4], pd[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // registers 8 sh + e, e + 1 are rows 16 sh + 8 (e >> 2) + 4 h + (e & 3), +1
-        const float la = e < 4 ? l0[e] : l1[e - 4], lb = e < 4 ? l0[e + 1] : l1[e - 3];
-        const float da = e < 4 ? d0[e] : d1[e - 4], dbv = e < 4 ? d0[e + 1] : d1[e - 3];
-        const float p0 = fast_exp2(__builtin_fmaf(s[8 * sh + e], c, -la));
-        const float p1 = fast_exp2(__builtin_fmaf(s[8 * sh + e + 1], c, -lb));
-        pp[e >> 1] = pack2_bf16(p0, p1);
-        pd[e >> 1] = pack2_bf16(p0 * (dp[8 * sh + e] - da), p1 * (dp[8 * sh + e + 1] - dbv));
+        for (int r = 0; r < 16; ++r) {
+          const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const bool ok = i < Lq && key < Lk && (!CAUSAL || key <= i + off);
+          s[r] = ok ? s[r] : kNegInf;
+          if constexpr (DO_K) dp[r] = ok ? dp[r] : 0.f;
+        }
       }
-      pf[sh] = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
-      dsf[sh] = __builtin_bit_cast(bf16x8, u32x4{pd[0], pd[1], pd[2], pd[3]});
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (D x 32 keys)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
+      bf16x8 pf[2], dsf[2];
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Gs, to, db, sh), pf[sh], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Qs, to, db, sh), dsf[sh], dk[db], 0, 0, 0);
+        const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 4 * h);
+        const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 8 + 4 * h);
+        f32x4 d0{}, d1{};
+        if constexpr (DO_K) {
+          d0 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 4 * h);
+          d1 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 8 + 4 * h);
+        }
+        uint32_t pp[4], pd[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          // registers 8 sh + e, e + 1 are rows 16 sh + 8 (e >> 2) + 4 h + (e & 3), +1
+          const float la = e < 4 ? l0[e] : l1[e - 4], lb = e < 4 ? l0[e + 1] : l1[e - 3];
+          const float p0 = fast_exp2(__builtin_fmaf(s[8 * sh + e], c, -la));
+          const float p1 = fast_exp2(__builtin_fmaf(s[8 * sh + e + 1], c, -lb));
+          if constexpr (DO_V) pp[e >> 1] = pack2_bf16(p0, p1);
+          if constexpr (DO_K) {
+            const float da = e < 4 ? d0[e] : d1[e - 4], dbv = e < 4 ? d0[e + 1] : d1[e - 3];
+            pd[e >> 1] = pack2_bf16(p0 * (dp[8 * sh + e] - da), p1 * (dp[8 * sh + e + 1] - dbv));
+          }
+        }
+        if constexpr (DO_V) pf[sh] = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
+        if constexpr (DO_K) dsf[sh] = __builtin_bit_cast(bf16x8, u32x4{pd[0], pd[1], pd[2], pd[3]});
       }
-  }
-  wait_vm_lds<0>();
+      // dV^T += dO^T P and dK^T += Q^T dS (D x 32 keys)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          if constexpr (DO_V)
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Gs, to, db, sh), pf[sh], dv[db], 0, 0, 0);
+          if constexpr (DO_K)
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Qs, to, db, sh), dsf[sh], dk[db], 0, 0, 0);
+        }
+    }
+    // every copy has landed and every LDS read is done; after the barrier
+    // the next pass may refill the stages
+    wait_vm_lds<0>();
+    __builtin_amdgcn_s_barrier();
 
-  if (key < Tk) {
-    const size_t kb = ((size_t)b * Hkv + hk) * (size_t)Tk + key;
-    u16* krow = dK + kb * D;
-    u16* vrow = dV + kb * D;
+    if (key < Tk) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * h;
-        u32x2 a, v2;
-        a[0] = pack2_bf16(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale);
-        a[1] = pack2_bf16(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale);
-        v2[0] = pack2_bf16(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
-        v2[1] = pack2_bf16(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
-        *reinterpret_cast<u32x2*>(krow + d0) = a;
-        *reinterpret_cast<u32x2*>(vrow + d0) = v2;
-      }
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * db + 8 * g4 + 4 * h;
+          if constexpr (DO_K) {
+            u32x2 a;
+            a[0] = pack2_bf16(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale);
+            a[1] = pack2_bf16(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale);
+            *reinterpret_cast<u32x2*>(dK + krow * D + d0) = a;
+          }
+          if constexpr (DO_V) {
+            u32x2 v2;
+            v2[0] = pack2_bf16(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
+            v2[1] = pack2_bf16(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
+            *reinterpret_cast<u32x2*>(dV + krow * D + d0) = v2;
+          }
+        }
+    }
+  };
+  if constexpr (SPLIT) {
+    run(std::integral_constant<int, 0>{});
+    run(std::integral_constant<int, 1>{});
+  } else {
+    run(std::integral_constant<int, 2>{});
   }
 }
 
