@@ -58,6 +58,18 @@ def _forced(row):
     _lib.attn_set_tile_table([row])
 
 
+# a candidate replaces the built-in choice only when it is faster by more
+# than this fraction (smaller differences are within run-to-run noise)
+MARGIN = 0.02
+
+
+def _conservative(times, builtin):
+    best = min(times, key=times.get)
+    if builtin in times and times[best] >= (1.0 - MARGIN) * times[builtin]:
+        return builtin
+    return best
+
+
 def tune_fwd(dtype, D, causal, reps):
     entries = []
     for lo, hi, wg in FWD_BUCKETS:
@@ -73,12 +85,17 @@ def tune_fwd(dtype, D, causal, reps):
             q, k, v = (workloads.randn_bf16((B, H, T, D), g, device="cuda") for _ in range(3))
             call = lambda: fwd(q, k, v, causal=bool(causal))  # noqa: E731
         size = math.ceil(T / 256) * B * H
-        cands = [(0, z) for z in ((0, 1) if causal else (0,))] + [(1, z) for z in ((0, 1) if causal else (0,))]
+        # zig-zag pairing is only offered where the 128-row grid is resident
+        # at once (size <= 256): elsewhere it only scatters the order in
+        # which K/V tiles are reused from L2 (measured: 2.3x the HBM traffic
+        # of the long prefill at equal speed)
+        zigs = (-1, 0, 1) if causal and size <= 256 else (-1,)
+        cands = [(shape, z) for shape in (0, 1) for z in zigs]
         times = {}
         for shape, zig in cands:
             _forced([tiles.OPS["fwd"], tiles.DTYPES[dtype], D, causal, 0, 2**31 - 1, shape, zig])
             times[f"{shape},{zig}"] = round(_time(call, reps, 10), 5)
-        best = min(times, key=times.get)
+        best = _conservative(times, f"{0 if size >= 512 else 1},-1")
         entries.append(dict(op="fwd", dtype=dtype, D=D, causal=causal, size_lo=lo, size_hi=hi,
                             choice=[int(x) for x in best.split(",")], times_ms=times,
                             problem=dict(B=B, Hq=H, Hkv=H, Tq=T, Tk=T, size=size)))
@@ -109,7 +126,7 @@ def tune_decode(dtype, D, reps):
         for per_cu in (1, 2, 3, 4):
             _forced([tiles.OPS["decode"], tiles.DTYPES[dtype], D, 1, 0, 2**31 - 1, per_cu, 0])
             times[str(per_cu)] = round(_time(call, reps, 5), 5)
-        best = min(times, key=times.get)
+        best = _conservative(times, "2")
         entries.append(dict(op="decode", dtype=dtype, D=D, causal=1, size_lo=lo, size_hi=hi,
                             choice=[int(best), 0], times_ms=times,
                             problem=dict(B=B, Hq=Hq, Hkv=Hkv, S_max=S, lengths="all S_max", size=size)))

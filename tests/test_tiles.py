@@ -87,9 +87,10 @@ def test_packaged_table_loads_and_is_applied():
     tiles.apply_default()
     assert _lib.attn_tile_table_size() == len(rows)
     for e, r in zip(doc["entries"], rows):
-        # the recorded choice is the fastest recorded candidate
-        best = min(e["times_ms"], key=e["times_ms"].get)
-        assert [int(x) for x in best.split(",")] == [r[6], r[7]] if e["op"] == "fwd" else int(best) == r[6]
+        # the recorded choice is a measured candidate within 2% of the fastest
+        t = e["times_ms"]
+        key = f"{r[6]},{r[7]}" if e["op"] == "fwd" else str(r[6])
+        assert key in t and t[key] <= min(t.values()) / (1.0 - 0.02) + 1e-9
         assert _lib.attn_tile_choice(r[0], r[1], r[2], r[3], r[4]) == (r[6], r[7])
     # buckets of one key do not overlap
     keys = {}
