@@ -601,7 +601,8 @@ def main():
                                    ms_per_step=round(pms, 5), flops_per_step=pf["flops"], dtype="e4m3",
                                    roofline=dict(bound="mfma", achieved=round(ptf, 3),
                                                  peak=round(PEAK_FP8_BF16_TFLOPS, 1), unit="TFLOP/s",
-                                                 frac=round(ptf / PEAK_FP8_BF16_TFLOPS, 4), traffic=None,
+                                                 frac=round(ptf / PEAK_FP8_BF16_TFLOPS, 4),
+                                                 traffic=traffic_for("fwd_bf16_kernel", "causal-fp8"),
                                                  kernel="fwd_bf16_kernel (E4M3 instance)",
                                                  peak_note="Q K^T on fp8 (5033 TFLOP/s), P V on bf16 (2517)"))
         del pf, prun
