@@ -58,7 +58,12 @@ struct FwdCfg {
   // 64-key tiles, 3-4 stages (64-96 KiB).  Two key groups: two stages each
   // within 64-80 KiB in all, so that two workgroups share a CU.
   static constexpr int BN = (KSPLIT > 1 && D == 128) ? 32 : 64;
-  static constexpr int NS = ((KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3)) + (FP8 ? 1 : 0);
+  // one key group, bf16, D=128: the loop is software-pipelined (the scores
+  // of tile j+1 are computed next to the softmax of tile j), so the K half
+  // of a tile is read one iteration earlier and the ring keeps one more
+  // stage (4 x 32 KiB)
+  static constexpr bool PIPE = !FP8 && KSPLIT == 1 && D == 128;
+  static constexpr int NS = PIPE ? 4 : ((KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3)) + (FP8 ? 1 : 0);
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int BM = 32 * NWG;               // query rows per workgroup
   static constexpr int NT = 64 * NW;                // threads per workgroup
@@ -211,33 +216,42 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // Q fragments (B operand of S^T = K Q^T), row qrow.  bf16: columns
   // 16 ks + 8 h .. +7.  E4M3: bytes 64 kk + 32 h .. +31; the K fragments
   // use the same bytes of their rows, so every column is paired once.
+  // Lanes past Tq read row Tq-1 (their results are never stored), so the
+  // loads are unconditional and issue back to back.  A negative score
+  // factor flips the sign bits of Q, after the first K/V copies are issued
+  // (flip_q below), so that waiting for Q does not hold up those copies.
   bf16x8 qf[FP8 ? 1 : C::KS];
   i32x8 qf8[FP8 ? C::KK : 1];
   {
-    const bool ok = qrow < Tq;
+    const int qsrc = min(qrow, Tq - 1);
     if constexpr (FP8) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)(ok ? qrow : 0) * D + 32 * h);
-      const uint32_t flip = negq ? 0x80808080u : 0u;
+      const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)qsrc * D + 32 * h);
 #pragma unroll
       for (int kk = 0; kk < C::KK; ++kk) {
-        u32x4 x0 = ok ? src[4 * kk] : u32x4{0u, 0u, 0u, 0u};
-        u32x4 x1 = ok ? src[4 * kk + 1] : u32x4{0u, 0u, 0u, 0u};
-        x0 ^= flip;
-        x1 ^= flip;
+        const u32x4 x0 = src[4 * kk];
+        const u32x4 x1 = src[4 * kk + 1];
         qf8[kk] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                         (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
       }
     } else {
-      const u32x4* src = reinterpret_cast<const u32x4*>(Qp + ((size_t)(ok ? qrow : 0) * D + 8 * h) * 2);
-      const uint32_t flip = negq ? 0x80008000u : 0u;
+      const u32x4* src = reinterpret_cast<const u32x4*>(Qp + ((size_t)qsrc * D + 8 * h) * 2);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
+    }
+  }
+  auto flip_q = [&]() {
+    if constexpr (FP8) {
+#pragma unroll
+      for (int kk = 0; kk < C::KK; ++kk) qf8[kk] ^= (int)0x80808080u;
+    } else {
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        u32x4 x = ok ? src[2 * ks] : u32x4{0u, 0u, 0u, 0u};
-        x ^= flip;
+        u32x4 x = __builtin_bit_cast(u32x4, qf[ks]);
+        x ^= 0x80008000u;
         qf[ks] = __builtin_bit_cast(bf16x8, x);
       }
     }
-  }
+  };
 
   u16* ring = smem + kg * C::RING;
   uint8_t* ring8 = reinterpret_cast<uint8_t*>(ring);
@@ -250,23 +264,32 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // lane l lands at byte 16 l of it, i.e. at (row, slot), and fetches the
   // chunk that the swizzle stores in that slot (the E4M3 V tile is stored
   // as is: it is only read back row by row for widening).  Rows at or past
-  // Lk are replaced by row Lk-1 (finite data; those keys are masked).
+  // Lk are replaced by row Lk-1 (finite data; those keys are masked).  The
+  // row and in-row byte offset of each lane's chunk are fixed per copy slot.
+  constexpr int CPR = D * C::ESZ / 16;   // 16-byte chunks per row
+  int dma_row[C::VMEM_PER_TILE], dma_col[C::VMEM_PER_TILE];
+#pragma unroll
+  for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
+    const int ci = (wg + NWG * i) % (2 * C::LOADS);
+    const int t = ci / C::LOADS, li = ci - t * C::LOADS;
+    const int p = li * 64 + lane;
+    const int r = p / CPR, slot = p % CPR;
+    int ch;
+    if constexpr (FP8)
+      ch = t ? slot : slot ^ swz_k8<D>(r);
+    else
+      ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
+    dma_row[i] = r;
+    dma_col[i] = ch * 16;
+  }
   auto issue = [&](int lt, int st) {
     const int kbase = (t_begin + lt) * C::BN;
-    constexpr int CPR = D * C::ESZ / 16;   // 16-byte chunks per row
 #pragma unroll
     for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
       const int ci = (wg + NWG * i) % (2 * C::LOADS);
       const int t = ci / C::LOADS, li = ci - t * C::LOADS;
-      const int p = li * 64 + lane;
-      const int r = p / CPR, slot = p % CPR;
-      int ch;
-      if constexpr (FP8)
-        ch = t ? slot : slot ^ swz_k8<D>(r);
-      else
-        ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
-      const int key = min(kbase + r, Lk - 1);
-      const uint8_t* g = (t ? Vp : Kp) + (size_t)key * D * C::ESZ + ch * 16;
+      const int key = min(kbase + dma_row[i], Lk - 1);
+      const uint8_t* g = (t ? Vp : Kp) + (size_t)key * D * C::ESZ + dma_col[i];
       __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)(ring8 + (st * 2 + t) * C::TB + li * 1024), 16, 0, 0);
     }
   };
@@ -301,13 +324,13 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   float m = kNegInf;   // reference maximum of scale*log2(e)*s for this lane's row
   float lsum = 0.f;    // running sum over this lane's half of the keys
 
-  f32x16 s[C::KB];
+  f32x16 s[C::PIPE ? 2 : 1][C::KB];
   bf16x8 pf[C::KB][2];
 
   // ---- S^T = K Q^T for the tile in stage st
-  auto do_scores = [&](int st) {
+  auto do_scores = [&](int st, f32x16* sd) {
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < C::KB; ++kb) sd[kb] = f32x16{};
     if constexpr (FP8) {
       // v_mfma_f32_32x32x64_f8f6f4 on E4M3 A and B (format 0 for both), no
       // block scale: exact products of the codes, fp32 sums
@@ -322,7 +345,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
           const u32x4 x1 = *(const __attribute__((address_space(3))) u32x4*)(k1 + 32 * kb * D);
           const i32x8 a = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3],
                                 (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[kk], s[kb], 0, 0, 0, 0, 0, 0);
+          sd[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf8[kk], sd[kb], 0, 0, 0, 0, 0, 0);
         }
       }
       return;
@@ -336,13 +359,13 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
         const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(kp + 32 * kb * D);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+        sd[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sd[kb], 0, 0, 0);
       }
     }
   };
 
-  // ---- mask, online-softmax update and P for the tile starting at key kbase
-  auto do_softmax = [&](int kbase) {
+  // ---- mask and online-softmax maximum for the tile starting at key kbase
+  auto do_max = [&](f32x16* sd, int kbase) {
     const bool need_mask = kbase + C::BN - 1 > kfull;
     if (need_mask) {
       const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
@@ -351,14 +374,14 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          s[kb][r] = key <= lim ? s[kb][r] : kNegInf;
+          sd[kb][r] = key <= lim ? sd[kb][r] : kNegInf;
         }
     }
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sd[kb][r]), sd[kb][r + 1]);
     mx = xhalf_max(mx);
     const float mt = (mx == kNegInf) ? kNegInf : mx * c;
     const bool grow = mt > m + kThresh;
@@ -370,6 +393,10 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
     }
+  };
+
+  // ---- P = exp2(c s - m) and its row sums
+  auto do_exp = [&](f32x16* sd) {
     const float nm = (m == kNegInf) ? 0.f : -m;
     float ls = lsum;
 #pragma unroll
@@ -380,8 +407,8 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * sh + e], c, nm));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * sh + e + 1], c, nm));
+          const float p0 = fast_exp2(__builtin_fmaf(sd[kb][8 * sh + e], c, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(sd[kb][8 * sh + e + 1], c, nm));
           ls += p0;
           ls += p1;
           pk[e >> 1] = pack2_bf16(p0, p1);
@@ -430,43 +457,87 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 
   // ---- main loop.  Every key group runs `per` iterations, so that all
   // waves meet the same barriers; a group with a shorter share idles
-  // through its last iteration.
+  // through its last iteration.  The first NS-1 stages are always filled
+  // (past the group's keys with copies of row Lk-1, never read), so that
+  // the number of copies in flight here is fixed and the wait for the Q
+  // loads above does not also wait for them.
+  // (A workgroup with no keys at all, e.g. query rows past a sequence's
+  // length, skips straight to the epilogue.)
+  if (ntiles_all > 0) {
 #pragma unroll
-  for (int p = 0; p < C::NS - 1; ++p)
-    if (p < ntiles) issue(p, p);
-  if constexpr (FP8) {
-    // widen tile 0 once every wave's copies of it have landed
-    if (ntiles > 0) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1);
+  for (int p = 0; p < C::NS - 1; ++p) issue(p, p);
+  if (negq) flip_q();
+  if constexpr (C::PIPE) {
+    // Iteration lt computes P of tile lt, the scores of tile lt+1 and
+    // O += V P of tile lt in one stretch of code with no branch, so that
+    // the exponentials (VALU) can issue between the score MFMAs, then masks
+    // tile lt+1 and updates the row maximum.  A wave whose last tile is lt
+    // still computes (and drops) scores from stage (lt+1) % NS: that stage
+    // is not being copied into, so this only costs time.
+    auto kb_of = [&](int lt) { return (t_begin + lt) * C::BN; };
+    wait_vm_lds<C::VMEM_PER_TILE * (C::NS - 2)>();   // tile 0
     __builtin_amdgcn_s_barrier();
-    if (ntiles > 0) widen(0, 0);
-  }
-  for (int lt = 0; lt < per; ++lt) {
-    const int st = lt % C::NS;
-    // bf16: this wave's copies of tile lt have landed and its LDS reads of
-    // tile lt-1 are done; after the barrier the same holds for every wave,
-    // so stage (lt-1) % NS can be refilled with tile lt+NS-1.  E4M3: the
-    // same one tile ahead (tile lt+1 is widened in this iteration; tile lt
-    // was widened in the previous one, its writes done before the barrier).
-    if constexpr (FP8) {
+    if (ntiles > 0 && kb_of(0) <= kmax) {
+      do_scores(0, s[0]);
+      do_max(s[0], kb_of(0));
+    }
+    auto step = [&](int lt, f32x16* sc, f32x16* sn) {
+      // this wave's copies of tile lt+1 have landed and its LDS reads of
+      // iteration lt-1 are done; after the barrier the same holds for every
+      // wave, so stage (lt-1) % NS can be refilled with tile lt+NS-1
       if (lt + 1 < ntiles)
         wait_tile<C::VMEM_PER_TILE, C::NS - 3>(ntiles - 2 - lt);
       else
         wait_lds();
-    } else {
-      if (lt < ntiles) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - lt);
+      __builtin_amdgcn_s_barrier();
+      if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
+      if (lt >= ntiles || kb_of(lt) > kmax) return;   // wave-uniform
+      do_exp(sc);
+      do_scores((lt + 1) % C::NS, sn);
+      do_pv(ring + ((lt % C::NS) * 2 + 1) * C::TILE);
+      if (lt + 1 < ntiles && kb_of(lt + 1) <= kmax) do_max(sn, kb_of(lt + 1));
+    };
+    for (int lt = 0; lt < per; lt += 2) {
+      step(lt, s[0], s[1]);
+      if (lt + 1 < per) step(lt + 1, s[1], s[0]);
     }
-    __builtin_amdgcn_s_barrier();
-    if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
-    if constexpr (FP8)
-      if (lt + 1 < ntiles) widen((lt + 1) % C::NS, (lt + 1) & 1);
-    const int kbase = (t_begin + lt) * C::BN;
-    if (lt >= ntiles || kbase > kmax) continue;   // wave-uniform: nothing of this tile for the wave
-    do_scores(st);
-    do_softmax(kbase);
-    if constexpr (FP8)
-      do_pv(vwide + (lt & 1) * C::TILE);
-    else
-      do_pv(ring + (st * 2 + 1) * C::TILE);
+  } else {
+    if constexpr (FP8) {
+      // widen tile 0 once every wave's copies of it have landed
+      wait_vm_lds<C::VMEM_PER_TILE * (C::NS - 2)>();
+      __builtin_amdgcn_s_barrier();
+      if (ntiles > 0) widen(0, 0);
+    }
+    for (int lt = 0; lt < per; ++lt) {
+      const int st = lt % C::NS;
+      // bf16: this wave's copies of tile lt have landed and its LDS reads of
+      // tile lt-1 are done; after the barrier the same holds for every wave,
+      // so stage (lt-1) % NS can be refilled with tile lt+NS-1.  E4M3: the
+      // same one tile ahead (tile lt+1 is widened in this iteration; tile lt
+      // was widened in the previous one, its writes done before the barrier).
+      if constexpr (FP8) {
+        if (lt + 1 < ntiles)
+          wait_tile<C::VMEM_PER_TILE, C::NS - 3>(ntiles - 2 - lt);
+        else
+          wait_lds();
+      } else {
+        if (lt < ntiles) wait_tile<C::VMEM_PER_TILE, C::NS - 2>(ntiles - 1 - lt);
+      }
+      __builtin_amdgcn_s_barrier();
+      if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
+      if constexpr (FP8)
+        if (lt + 1 < ntiles) widen((lt + 1) % C::NS, (lt + 1) & 1);
+      const int kbase = (t_begin + lt) * C::BN;
+      if (lt >= ntiles || kbase > kmax) continue;   // wave-uniform: nothing of this tile for the wave
+      do_scores(st, s[0]);
+      do_max(s[0], kbase);
+      do_exp(s[0]);
+      if constexpr (FP8)
+        do_pv(vwide + (lt & 1) * C::TILE);
+      else
+        do_pv(ring + (st * 2 + 1) * C::TILE);
+    }
+  }
   }
 
   // ---- merge of the key groups' partials into group 0: with the combined
