@@ -164,21 +164,37 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   const int kg = w / NWG;          // key group
   const int wg = w - kg * NWG;     // wave within the group = its 32-row block
 
-  // Workgroup -> (query tile, batch, head).  The query-tile index is the slow
-  // one and runs from the last tile down, so under a causal mask the longest
-  // tiles start first; ids sharing a (batch, head) are B*Hq apart, which puts
-  // them on the same XCD (and L2) whenever B*Hq is a multiple of 8.  When
-  // the whole grid is resident at once (zig), workgroups id and id + grid/2
-  // share a CU, so the second half of the ids runs from the first tile up:
-  // each CU then holds a long and a short causal tile, equal work in all.
+  // Workgroup -> (query tile, batch, head).  Query tiles run from the last
+  // tile down, so under a causal mask the longest tiles start first.  When
+  // the number of (batch, KV head) units is a multiple of 8, each XCD gets
+  // whole units (below); otherwise the query-tile index is the slow one and
+  // ids sharing a (batch, head) are B*Hq apart.  When the whole grid is
+  // resident at once (zig), workgroups id and id + grid/2 share a CU, so the
+  // second half of the ids runs from the first tile up: each CU then holds a
+  // long and a short causal tile, equal work in all.
   const int BH = B * Hq;
   const int id = blockIdx.x;
-  const int tq_slot = id / BH;
+  const int G = Hq / Hkv, NU = B * Hkv;
+  int tq_slot, b, hq;
+  if (!zig && NU % 8 == 0) {
+    // ids i, i+8, i+16, ... run on one XCD: give each XCD whole (batch, KV
+    // head) units, one unit's query heads and tiles after another, so that
+    // the workgroups resident on an XCD at once share one head's K/V in L2
+    const int xcd = id & 7, k = id >> 3;
+    const int ul = k / (G * nqt), r = k - ul * (G * nqt);
+    tq_slot = r / G;
+    const int u = xcd + 8 * ul;
+    b = u / Hkv;
+    hq = (u - b * Hkv) * G + (r - tq_slot * G);
+  } else {
+    tq_slot = id / BH;
+    const int bh = id - tq_slot * BH;
+    b = bh / Hq;
+    hq = bh - b * Hq;
+  }
   const int half = (nqt + 1) / 2;
   const int qt = (zig && tq_slot >= half) ? tq_slot - half : nqt - 1 - tq_slot;
-  const int bh = id - tq_slot * BH;
-  const int b = bh / Hq, hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
+  const int hk = hq / G;
 
   int Lk = Tk, Lq = Tq;
   if (kv_lens != nullptr) {

@@ -177,6 +177,15 @@ def test_gqa_groups(G):
     run_case(2, 8, 8 // G, 200, 200, 128, torch.bfloat16, True, seed=10 + G)
 
 
+@pytest.mark.parametrize("D,causal", [(64, False), (128, True), (128, False)])
+def test_unit_order_covers_every_tile(D, causal):
+    """With a multiple of 8 (batch, KV head) units the workgroups are
+    ordered unit by unit on each XCD; every query tile of every query head
+    (GQA: 4 per KV head) must still be computed exactly once.  Full output
+    against the oracle."""
+    run_case(2, 16, 4, 600, 600, D, torch.bfloat16, causal, seed=31)
+
+
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("B,Hq,Hkv", [(1, 8, 2), (2, 32, 8)])
