@@ -192,7 +192,8 @@ template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
-    u16* __restrict__ dQ, int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, float scale, int negk) {
+    u16* __restrict__ dQ, int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, float scale, int negk,
+    int uorder) {
   constexpr int BN = 32, NS = 3, KS = D / 16, DB = D / 32, BM = 32 * NW;
   constexpr int TILE = BN * D;
   constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW, VM_PER_TILE = 2 * PER;
@@ -201,12 +202,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BH = B * Hq;
-  const int tq_slot = blockIdx.x / BH;
+  // workgroup -> (query tile, batch, head): heaviest tiles first; for grids
+  // of several rounds with a multiple of 8 (batch, KV head) units (uorder)
+  // each XCD takes whole units, so its resident workgroups stream one
+  // head's K/V through L2 together
+  const int G = Hq / Hkv, NU = B * Hkv;
+  const int id = blockIdx.x;
+  int tq_slot, b, hq;
+  if (uorder) {
+    const int k = id >> 3, ul = k / (G * nqt), r = k - ul * (G * nqt);
+    tq_slot = r / G;
+    const int u = (id & 7) + 8 * ul;
+    b = u / Hkv;
+    hq = (u - b * Hkv) * G + (r - tq_slot * G);
+  } else {
+    const int BH = B * Hq;
+    tq_slot = id / BH;
+    const int bh = id - tq_slot * BH;
+    b = bh / Hq;
+    hq = bh - b * Hq;
+  }
   const int qt = nqt - 1 - tq_slot;
-  const int bh = blockIdx.x - tq_slot * BH;
-  const int b = bh / Hq, hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
+  const int hk = hq / G;
   int Lq, Lk;
   valid_lengths(kv_lens, b, Tq, Tk, Lq, Lk);
   const int off = Lk - Lq;
@@ -326,7 +343,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
-    int negk) {
+    int negk, int uorder) {
   constexpr int BMQ = 32, NS = 3, KS = D / 16, DB = D / 32, BNK = 32 * NW;
   constexpr int TILE = BMQ * D;
   constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW;
@@ -338,11 +355,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int BH = B * Hkv;
-  const int kt_slot = blockIdx.x / BH;
-  const int kt = kt_slot;
-  const int bh = blockIdx.x - kt_slot * BH;
-  const int b = bh / Hkv, hk = bh - b * Hkv;
+  // workgroup -> (key tile, batch, KV head); as for dQ, with uorder each
+  // XCD takes whole units, so its resident workgroups stream one unit's Q
+  // and dO through L2 together
+  const int NU = B * Hkv;
+  const int id = blockIdx.x;
+  int kt, b, hk;
+  if (uorder) {
+    const int nkt = (int)(gridDim.x / NU);
+    const int k = id >> 3, ul = k / nkt;
+    kt = k - ul * nkt;
+    const int u = (id & 7) + 8 * ul;
+    b = u / Hkv;
+    hk = u - b * Hkv;
+  } else {
+    kt = id / NU;
+    const int bh = id - kt * NU;
+    b = bh / Hkv;
+    hk = bh - b * Hkv;
+  }
   const int G = Hq / Hkv;
   int Lq, Lk;
   valid_lengths(kv_lens, b, Tq, Tk, Lq, Lk);
@@ -523,6 +554,11 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
   float* Lc = a.ws + rows;
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 1e-30f);
   const int negk = a.scale < 0.f ? 1 : 0;
+  // per-XCD unit order of the dQ and dK/dV workgroups once a grid takes
+  // several rounds (smaller grids keep the heavy-first order across heads)
+  auto uorder = [&](long long grid) {
+    return ((a.B * a.Hkv) % 8 == 0 && grid >= 4LL * device_cu_count()) ? 1 : 0;
+  };
   {
     const long long grid = (rows + 31) / 32;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -537,7 +573,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDqWaves), 0, st,
                        (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens,
-                       (u16*)a.dq, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, a.scale, negk);
+                       (u16*)a.dq, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, a.scale, negk, uorder(grid));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -547,7 +583,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDkdvWaves), 0, st,
                        (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens,
-                       (u16*)a.dk, (u16*)a.dv, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nkt, c, a.scale, negk);
+                       (u16*)a.dk, (u16*)a.dv, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nkt, c, a.scale, negk, uorder(grid));
   }
   return hipGetLastError();
 }

@@ -151,7 +151,7 @@ template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
 __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
     u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
-    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int zig, float oscale) {
+    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int zig, int uorder, float oscale) {
   using C = FwdCfg<D, NWG, KSPLIT, FP8>;
   const uint8_t* __restrict__ Q = static_cast<const uint8_t*>(Qv);
   const uint8_t* __restrict__ K = static_cast<const uint8_t*>(Kv);
@@ -165,10 +165,11 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   const int wg = w - kg * NWG;     // wave within the group = its 32-row block
 
   // Workgroup -> (query tile, batch, head).  Query tiles run from the last
-  // tile down, so under a causal mask the longest tiles start first.  When
-  // the number of (batch, KV head) units is a multiple of 8, each XCD gets
-  // whole units (below); otherwise the query-tile index is the slow one and
-  // ids sharing a (batch, head) are B*Hq apart.  When the whole grid is
+  // tile down, so under a causal mask the longest tiles start first.  For
+  // grids of several rounds whose (batch, KV head) unit count is a multiple
+  // of 8 (uorder), each XCD gets whole units (below); otherwise the
+  // query-tile index is the slow one and ids sharing a (batch, head) are
+  // B*Hq apart.  When the whole grid is
   // resident at once (zig), workgroups id and id + grid/2 share a CU, so the
   // second half of the ids runs from the first tile up: each CU then holds a
   // long and a short causal tile, equal work in all.
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   const int id = blockIdx.x;
   const int G = Hq / Hkv, NU = B * Hkv;
   int tq_slot, b, hq;
-  if (!zig && NU % 8 == 0) {
+  if (uorder) {
     // ids i, i+8, i+16, ... run on one XCD: give each XCD whole (batch, KV
     // head) units, one unit's query heads and tiles after another, so that
     // the workgroups resident on an XCD at once share one head's K/V in L2
@@ -659,8 +660,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t st, int zig_choice) {
   // heavy-first order is kept.  The launch table may force it either way.
   const int zig = zig_choice >= 0 ? zig_choice
                                   : ((CAUSAL && D == 64 && grid <= 2LL * device_cu_count()) ? 1 : 0);
+  // unit order per XCD (see the kernel) once the grid takes several rounds
+  const int uorder = (!zig && (a.B * a.Hkv) % 8 == 0 && grid >= 4LL * device_cu_count()) ? 1 : 0;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL, FP8>), dim3((unsigned)grid), dim3(C::NT), 0, st, a.q,
-                     a.k, a.v, (u16*)a.o, a.lse, a.kv_lens, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig,
+                     a.k, a.v, (u16*)a.o, a.lse, a.kv_lens, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig, uorder,
                      FP8 ? a.v_scale : 1.f);
   return hipGetLastError();
 }

@@ -129,6 +129,36 @@ def test_causal_workload_shape_rows_sampled():
     assert np.abs(dvs - want).max() <= TOL * float(np.abs(want).max())
 
 
+def test_unit_order_grids_rows_sampled():
+    """dQ and dK/dV grids of several rounds (2048 and 1024 workgroups) with a
+    multiple of 8 (batch, KV head) units take the per-XCD unit order.  One
+    dQ row of every (batch, query head, 128-row query tile) against the row
+    oracle; every key tile through the column sums the softmax Jacobian
+    fixes (sum_j dK_j = 0 and sum_j dV_j = sum of dO over the KV head's
+    query heads, per batch, KV head and column)."""
+    B, Hq, Hkv, T, D = 8, 32, 16, 1024, 64
+    q, k, v, do = gen((B, Hq, T, D), 51), gen((B, Hkv, T, D), 52), gen((B, Hkv, T, D), 53), gen((B, Hq, T, D), 54)
+    sc = 1.0 / math.sqrt(D)
+    o_ref, lse_ref = oracle.attention(q, k, v, sc, True)
+    dev = [x.cuda() for x in (q, k, v, torch.from_numpy(o_ref).to(torch.bfloat16),
+                             torch.from_numpy(lse_ref).to(torch.float32), do)]
+    dq, dk, dv = ea.bwd(*dev, causal=True, scale=sc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rows = [(b, h, t * 128 + int(rng.integers(128))) for b in range(B) for h in range(Hq) for t in range(T // 128)]
+    ref = oracle.backward_rows(q, k, v, do, rows, sc, True)
+    idx = tuple(torch.as_tensor(a, device="cuda") for a in np.array(rows).T)
+    got = dq[idx].float().cpu().double().numpy()
+    err = float(np.abs(got - ref).max())
+    print(f"  unit order dq rows: max err {err:.3e} (ref max {np.abs(ref).max():.3e})", flush=True)
+    assert err <= TOL * float(np.abs(ref).max())
+    dks = dk.float().sum(dim=2).cpu().double().numpy()
+    dvs = dv.float().sum(dim=2).cpu().double().numpy()
+    want = do.double().sum(dim=2).reshape(B, Hkv, Hq // Hkv, D).sum(dim=2).numpy()
+    assert np.abs(dks).max() <= TOL * float(dk.float().abs().max()) * 8
+    assert np.abs(dvs - want).max() <= TOL * float(np.abs(want).max())
+
+
 def test_deterministic():
     q, k, v, do = (gen((2, 4, 300, 128), s).cuda() for s in range(4))
     o, lse = ea.fwd(q, k, v, causal=True)
