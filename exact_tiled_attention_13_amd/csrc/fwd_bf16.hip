@@ -36,9 +36,9 @@
 // on almost every tile.
 //
 // K and V tiles (BN keys) are copied HBM -> LDS by global_load_lds_dwordx4
-// (no staging registers) into an NS-stage ring per key group: tiles
-// j+1 .. j+NS-1 are in flight while tile j is computed, and each wave waits
-// (vmcnt) only for the copies of the tile it is about to read.  Rows are
+// (no staging registers) into an NS-stage ring per key group: the copies
+// of the next tiles are in flight while a tile is computed, and each wave
+// waits (vmcnt) only for the copies of the tiles it is about to read.  Rows are
 // stored unpadded, with the 16-byte chunks of each row XOR-permuted (swz_k,
 // swz_v below) so that the 16-byte K reads and the transposing V reads are
 // free of bank conflicts.
@@ -55,8 +55,8 @@ struct FwdCfg {
   static constexpr int NW = NWG * KSPLIT;           // waves per workgroup
   // keys per tile and LDS stages per key group (tiles in flight + 1; E4M3
   // keeps one more stage, whose V tile is being widened).  One key group:
-  // 64-key tiles, 3-4 stages (64-96 KiB).  Two key groups: two stages each
-  // within 64-80 KiB in all, so that two workgroups share a CU.
+  // 64-key tiles, 3-4 stages (64-128 KiB).  Two key groups: two stages
+  // each within 64-80 KiB in all, so that two workgroups share a CU.
   static constexpr int BN = (KSPLIT > 1 && D == 128) ? 32 : 64;
   // one key group, bf16, D=128: the loop is software-pipelined (the scores
   // of tile j+1 are computed next to the softmax of tile j), so the K half
