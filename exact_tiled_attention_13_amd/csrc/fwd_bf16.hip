@@ -9,9 +9,9 @@
 //
 // gfx950 mapping.  A workgroup owns BM = 32*NWG query rows of one (batch,
 // query head).  Its waves form KSPLIT key groups of NWG waves: every group
-// covers all BM rows (32 per wave) over its own contiguous share of the key
-// range, and the groups' partial (m, l, O) are merged through LDS at the end
-// with the same rescale rule.  KSPLIT > 1 shortens the chain of key tiles a
+// covers all BM rows (32 per wave) over its own share of the key tiles
+// (every KSPLIT-th tile), and the groups' partial (m, l, O) are merged
+// through LDS at the end with the same rescale rule.  KSPLIT > 1 shortens the chain of key tiles a
 // workgroup walks through, for grids too small to fill the chip.  Each wave
 // works in the transposed frame, where every lane owns one query row:
 //
@@ -212,15 +212,19 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   u16* Op = O + ((size_t)b * Hq + hq) * (size_t)Tq * D;
 
   // keys the workgroup needs: [0, kend) = ntiles_all tiles; key group g
-  // takes tiles [g * per, min((g + 1) * per, ntiles_all))
+  // takes tiles g, g + KSPLIT, g + 2 KSPLIT, ... (its tile lt is key tile
+  // tile_of(lt)).  Interleaved shares keep the workgroups of one head on
+  // the same key tiles at the same time, so a grid that starts all at once
+  // fetches each tile from HBM once and the rest from L2, and the causal
+  // diagonal tiles fall to both groups.
   int kend = 0;
   const int rows_end = min(q0 + C::BM, Lq);
   if (rows_end > q0) kend = CAUSAL ? min(Lk, rows_end + off) : Lk;
   if (kend < 0) kend = 0;
   const int ntiles_all = (kend + C::BN - 1) / C::BN;
   const int per = (ntiles_all + KSPLIT - 1) / KSPLIT;
-  const int t_begin = kg * per;
-  const int ntiles = max(0, min(per, ntiles_all - t_begin));
+  const int ntiles = ntiles_all > kg ? (ntiles_all - kg + KSPLIT - 1) / KSPLIT : 0;
+  auto tile_of = [&](int lt) { return lt * KSPLIT + kg; };
 
   // this wave's rows [wrow0, wrow0 + 32): last key any valid row may see
   // (kmax) and last key every row sees (kfull; past it a tile needs the mask)
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // E4M3: the widened bf16 V tiles follow the stages
   u16* vwide = ring + C::NS * C::TB;
 
-  // HBM -> LDS copy of the group's tile lt (key tile t_begin + lt) into
+  // HBM -> LDS copy of the group's tile lt (key tile tile_of(lt)) into
   // stage st.  The tile's 2 LOADS wave-loads (K, then V) are dealt out to
   // the group's waves.  Each 1 KiB wave-load covers 1024 / (D ESZ) rows;
   // lane l lands at byte 16 l of it, i.e. at (row, slot), and fetches the
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     dma_col[i] = ch * 16;
   }
   auto issue = [&](int lt, int st) {
-    const int kbase = (t_begin + lt) * C::BN;
+    const int kbase = tile_of(lt) * C::BN;
 #pragma unroll
     for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
       const int ci = (wg + NWG * i) % (2 * C::LOADS);
@@ -491,7 +495,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     // tile lt+1 and updates the row maximum.  A wave whose last tile is lt
     // still computes (and drops) scores from stage (lt+1) % NS: that stage
     // is not being copied into, so this only costs time.
-    auto kb_of = [&](int lt) { return (t_begin + lt) * C::BN; };
+    auto kb_of = [&](int lt) { return tile_of(lt) * C::BN; };
     wait_vm_lds<C::VMEM_PER_TILE * (C::NS - 2)>();   // tile 0
     __builtin_amdgcn_s_barrier();
     if (ntiles > 0 && kb_of(0) <= kmax) {
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
       if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
       if constexpr (FP8)
         if (lt + 1 < ntiles) widen((lt + 1) % C::NS, (lt + 1) & 1);
-      const int kbase = (t_begin + lt) * C::BN;
+      const int kbase = tile_of(lt) * C::BN;
       if (lt >= ntiles || kbase > kmax) continue;   // wave-uniform: nothing of this tile for the wave
       do_scores(st, s[0]);
       do_max(s[0], kbase);
