@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // of several rounds with a multiple of 8 (batch, KV head) units (uorder)
   // each XCD takes whole units, so its resident workgroups stream one
   // head's K/V through L2 together
-  const int G = Hq / Hkv, NU = B * Hkv;
+  const int G = Hq / Hkv;
   const int id = blockIdx.x;
   int tq_slot, b, hq;
   if (uorder) {
@@ -362,7 +362,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int id = blockIdx.x;
   int kt, b, hk;
   if (uorder) {
-    const int nkt = (int)(gridDim.x / NU);
     const int k = id >> 3, ul = k / nkt;
     kt = k - ul * nkt;
     const int u = (id & 7) + 8 * ul;

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // long and a short causal tile, equal work in all.
   const int BH = B * Hq;
   const int id = blockIdx.x;
-  const int G = Hq / Hkv, NU = B * Hkv;
+  const int G = Hq / Hkv;
   int tq_slot, b, hq;
   if (uorder) {
     // ids i, i+8, i+16, ... run on one XCD: give each XCD whole (batch, KV
