@@ -2,7 +2,8 @@
 """Throughput of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload causal|long|ragged|decode|decode-paged|decode-fp8|single] [--backward]
+                    [--workload causal|long|ragged|decode|decode-paged|decode-fp8|causal-fp8|long-fp8|single]
+                    [--backward]
 
 A step is one pass of the hot path over one batch of synthetic, seeded input
 already resident in HBM.  The headline line measures the causal prefill
@@ -21,6 +22,12 @@ events recorded on the stream they run on.
 
 The float64 CPU oracle is timed on a bounded sample of the same workload
 (cpu_baseline).  It is a reported baseline, not the target.
+
+roofline.traffic (HBM bytes per launch) and roofline.mfma_busy (share of the
+chip's SIMD cycles with the matrix unit busy) come from rocprofv3 counter
+runs summarised into profiles/traffic.json and profiles/mfma.json
+(--summarize-pmc, --summarize-mfma); they are null once the kernel's sources
+differ from those the counters were taken on.
 """
 
 from __future__ import annotations
@@ -57,6 +64,12 @@ PEAK_FP8_TFLOPS = 5033.2    # 256 CU * 2.4 GHz * 8192 dense fp8 flop/clk/CU
 PEAK_FP8_BF16_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 PEAK_F32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+N_SIMD = 256 * 4            # SIMDs (matrix units) on the chip
+N_SE = 32                   # SQ_BUSY_CYCLES is summed over 8 XCDs x 4 shader engines
+# one rocprofv3 --pmc pass (7 SQ + 1 GRBM counters, within one pass's limits)
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                 "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_BUSY_CYCLES",
+                 "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE")
 CALLS_PER_GRAPH = 20
 
 
@@ -394,6 +407,73 @@ def traffic_for(kernel, workload):
     return entry["traffic_bytes_per_launch"]
 
 
+def mfma_busy_for(kernel, workload):
+    """Fraction of the chip's SIMD cycles whose matrix unit was busy during
+    the kernel, from the committed counter summary, or None when there is
+    none or the kernel's sources changed since it was taken."""
+    path = os.path.join(PROFILES, "mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        entry = json.load(fh).get(f"{kernel}/{workload}")
+    if not entry or entry.get("sources_sha256_16") != sources_hash(kernel):
+        return None
+    return round(entry["mfma_busy"], 4)
+
+
+def summarize_mfma(kernel, workload, pmc_dir, command):
+    """Turn one rocprofv3 --pmc run of MFMA_COUNTERS into an entry of
+    profiles/mfma.json: per dispatch of `kernel` (averaged), the cycles in
+    which the shader engines held waves (SQ_BUSY_CYCLES / engines), the
+    matrix units' busy fraction SQ_VALU_MFMA_BUSY_CYCLES / (those cycles x
+    SIMDs), the MFMA flops the instructions performed (MOPS x 512) against
+    the algorithmic flops, the share of MFMA-busy cycles in which a VALU
+    instruction also issued, and the clock implied by those cycles over the
+    dispatch's duration (the profiled run's own clock).  GRBM_GUI_ACTIVE is
+    kept for reference: on dispatches of a few microseconds it also counts
+    cycles outside the kernel's timestamps."""
+    rows = {}
+    durs = []
+    for f in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                rows.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "SQ_BUSY_CYCLES":
+                    durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9)
+    missing = [c for c in MFMA_COUNTERS if c not in rows]
+    if missing:
+        raise SystemExit(f"no rows for {missing} of {kernel} under {pmc_dir}")
+    mean = {c: sum(v) / len(v) for c, v in rows.items()}
+    cycles = mean["SQ_BUSY_CYCLES"] / N_SE
+    from exact_tiled_attention_13_amd import workloads as wl
+
+    W = wl.WORKLOADS[workload]
+    lens = None
+    if W.lens is not None:
+        lens = wl.draw_lengths(W.B, W.lens[0], W.lens[1], W.lens[2], 0)
+    f_alg = 4 * W.D * prefill_pairs(W.B, W.Hq, W.Tq, W.Tk, W.causal, lens)
+    mops = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + mean["SQ_INSTS_VALU_MFMA_MOPS_F8"] + \
+        mean["SQ_INSTS_VALU_MFMA_MOPS_F6F4"]
+    dur = sum(durs) / len(durs)
+    entry = dict(kernel=kernel, workload=workload, sources_sha256_16=sources_hash(kernel),
+                 dispatches=len(rows["SQ_BUSY_CYCLES"]), counters_per_dispatch=mean,
+                 active_cycles=cycles, mfma_busy=mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMD),
+                 coexec_of_busy=mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / mean["SQ_VALU_MFMA_BUSY_CYCLES"],
+                 mfma_flops=mops * 512, algorithmic_flops=f_alg, mfma_flops_over_algorithmic=mops * 512 / f_alg,
+                 dispatch_seconds=dur, implied_clock_ghz=cycles / dur / 1e9, command=command)
+    path = os.path.join(PROFILES, "mfma.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            data = json.load(fh)
+    data[f"{kernel}/{workload}"] = entry
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps(entry, indent=1))
+
+
 def copy_calibration(steps):
     """A plain copy of COPY_BYTES, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -469,7 +549,12 @@ def main():
                                                          "COPY_WRITE_DIR"),
                     help="write profiles/traffic.json from rocprofv3 --pmc output directories")
     ap.add_argument("--pmc-command", default="", help="command line recorded with --summarize-pmc")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("KERNEL", "PMC_DIR"),
+                    help="write profiles/mfma.json from a rocprofv3 --pmc run of MFMA_COUNTERS")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma[0], args.workload, args.summarize_mfma[1], args.pmc_command)
+        return
     if args.summarize_pmc:
         k, fd, wd, cfd, cwd = args.summarize_pmc
         summarize_pmc(k, args.workload, fd, wd, cfd, cwd, args.pmc_command)
@@ -554,7 +639,7 @@ def main():
                     flops_per_step=pre["flops"], parallelism="single GPU", launch_table=launch_table),
         roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=peak, unit="TFLOP/s",
                       frac=round(tflops / peak, 4), traffic=traffic_for(kname, args.workload), kernel=kname,
-                      kernel_ms=round(ms, 5)),
+                      kernel_ms=round(ms, 5), mfma_busy=mfma_busy_for(kname, args.workload)),
     )
     del pre, runner
     if args.workload == "causal" and not args.no_decode:
@@ -603,6 +688,7 @@ def main():
                                                  peak=round(PEAK_FP8_BF16_TFLOPS, 1), unit="TFLOP/s",
                                                  frac=round(ptf / PEAK_FP8_BF16_TFLOPS, 4),
                                                  traffic=traffic_for("fwd_bf16_kernel", "causal-fp8"),
+                                                 mfma_busy=mfma_busy_for("fwd_bf16_kernel", "causal-fp8"),
                                                  kernel="fwd_bf16_kernel (E4M3 instance)",
                                                  peak_note="Q K^T on fp8 (5033 TFLOP/s), P V on bf16 (2517)"))
         del pf, prun
