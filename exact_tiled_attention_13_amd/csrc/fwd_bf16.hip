@@ -58,11 +58,11 @@ struct FwdCfg {
   // 64-key tiles, 3-4 stages (64-128 KiB).  Two key groups: two stages
   // each within 64-80 KiB in all, so that two workgroups share a CU.
   static constexpr int BN = (KSPLIT > 1 && D == 128) ? 32 : 64;
-  // one key group, bf16, D=128: the loop is software-pipelined (the scores
-  // of tile j+1 are computed next to the softmax of tile j), so the K half
-  // of a tile is read one iteration earlier and the ring keeps one more
-  // stage (4 x 32 KiB)
-  static constexpr bool PIPE = !FP8 && KSPLIT == 1 && D == 128;
+  // one key group, D=128: the loop is software-pipelined (the scores of
+  // tile j+1 are computed next to the softmax of tile j), so the K half of
+  // a tile is read one iteration earlier and the ring keeps 4 stages (bf16
+  // 4 x 32 KiB; E4M3 4 x 16 KiB plus the two widened V tiles)
+  static constexpr bool PIPE = KSPLIT == 1 && D == 128;
   static constexpr int NS = PIPE ? 4 : ((KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3)) + (FP8 ? 1 : 0);
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int BM = 32 * NWG;               // query rows per workgroup
@@ -495,9 +495,13 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     // tile lt+1 and updates the row maximum.  A wave whose last tile is lt
     // still computes (and drops) scores from stage (lt+1) % NS: that stage
     // is not being copied into, so this only costs time.
+    // E4M3: iteration lt also widens the V tile of tile lt+1 (into the
+    // buffer P V of tile lt-1 read before this iteration's barrier).
     auto kb_of = [&](int lt) { return tile_of(lt) * C::BN; };
     wait_vm_lds<C::VMEM_PER_TILE * (C::NS - 2)>();   // tile 0
     __builtin_amdgcn_s_barrier();
+    if constexpr (FP8)
+      if (ntiles > 0) widen(0, 0);
     if (ntiles > 0 && kb_of(0) <= kmax) {
       do_scores(0, s[0]);
       do_max(s[0], kb_of(0));
@@ -512,10 +516,15 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
         wait_lds();
       __builtin_amdgcn_s_barrier();
       if (lt + C::NS - 1 < ntiles) issue(lt + C::NS - 1, (lt + C::NS - 1) % C::NS);
+      if constexpr (FP8)
+        if (lt + 1 < ntiles) widen((lt + 1) % C::NS, (lt + 1) & 1);
       if (lt >= ntiles || kb_of(lt) > kmax) return;   // wave-uniform
       do_exp(sc);
       do_scores((lt + 1) % C::NS, sn);
-      do_pv(ring + ((lt % C::NS) * 2 + 1) * C::TILE);
+      if constexpr (FP8)
+        do_pv(vwide + (lt & 1) * C::TILE);
+      else
+        do_pv(ring + ((lt % C::NS) * 2 + 1) * C::TILE);
       if (lt + 1 < ntiles && kb_of(lt + 1) <= kmax) do_max(sn, kb_of(lt + 1));
     };
     for (int lt = 0; lt < per; lt += 2) {
