@@ -634,9 +634,11 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   }
 
   // ---- epilogue: O = acc / l, LSE = ln(2) (m + log2 l); empty rows -> 0, -inf
+  // (selected, not multiplied by 0: a padding row's Q may hold NaN)
   const float ltot = xhalf_sum(lsum);
   const bool has = (qrow < Lq) && (ltot > 0.f);
   const float inv = has ? oscale / ltot : 0.f;
+  auto outv = [&](float x) { return has ? x * inv : 0.f; };
   if (qrow < Tq) {
     u16* orow = Op + (size_t)qrow * D;
 #pragma unroll
@@ -645,8 +647,8 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = 32 * db + 8 * g4 + 4 * h;
         u32x2 pk;
-        pk[0] = pack2_bf16(oacc[db][4 * g4 + 0] * inv, oacc[db][4 * g4 + 1] * inv);
-        pk[1] = pack2_bf16(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv);
+        pk[0] = pack2_bf16(outv(oacc[db][4 * g4 + 0]), outv(oacc[db][4 * g4 + 1]));
+        pk[1] = pack2_bf16(outv(oacc[db][4 * g4 + 2]), outv(oacc[db][4 * g4 + 3]));
         *reinterpret_cast<u32x2*>(orow + d0) = pk;
       }
     if (LSE != nullptr && h == 0)

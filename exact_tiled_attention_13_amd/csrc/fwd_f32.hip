@@ -175,14 +175,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   const float ltot = xhalf_sum(lsum);
   const bool has = (qrow < Lq) && (ltot > 0.f);
   const float inv = has ? 1.f / ltot : 0.f;
+  // selected, not multiplied by 0: a padding row's Q may hold NaN
+  auto outv = [&](float x) { return has ? x * inv : 0.f; };
   if (qrow < Tq) {
     float* orow = Op + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 v4 = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv, oacc[db][4 * g4 + 2] * inv,
-                    oacc[db][4 * g4 + 3] * inv};
+        f32x4 v4 = {outv(oacc[db][4 * g4]), outv(oacc[db][4 * g4 + 1]), outv(oacc[db][4 * g4 + 2]),
+                    outv(oacc[db][4 * g4 + 3])};
         *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g4 + 4 * h) = v4;
       }
     if (LSE != nullptr && h == 0)

@@ -130,11 +130,14 @@ def test_fp8_paged_decode(P, D):
 
 
 # ------------------------------------------------------------------ prefill
-def run_fwd(B, Hq, Hkv, Tq, Tk, D, causal, lens=None, scale=None, scales=(S0, S0, S0), seed=0, poison=False):
+def run_fwd(B, Hq, Hkv, Tq, Tk, D, causal, lens=None, scale=None, scales=(S0, S0, S0), seed=0, poison=False,
+            poison_q=False):
     q, k, v, sc = workloads.make_fwd_inputs_fp8(B, Hq, Hkv, Tq, Tk, D, seed=seed, scales=scales)
     if poison and lens is not None:
         workloads.poison_tail_(k.view(torch.uint8), lens, 0x7F)
         workloads.poison_tail_(v.view(torch.uint8), lens, 0x7F)
+    if poison_q and lens is not None:
+        workloads.poison_tail_(q.view(torch.uint8), lens, 0x7F)
     scale = 1 / np.sqrt(D) if scale is None else scale
     kv = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
     o, lse = ea.fwd_fp8(q.cuda(), k.cuda(), v.cuda(), q_scale=sc[0], k_scale=sc[1], v_scale=sc[2], causal=causal,
@@ -173,6 +176,16 @@ def test_fp8_prefill_padding(causal):
     lens = [1, 0, 300, 512, 77]
     o, lse, o_ref, l_ref = run_fwd(5, 4, 4, 512, 512, 64, causal, lens=lens, seed=3, poison=True)
     check(o, lse, o_ref, l_ref, f"fp8 padding causal{causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_prefill_padding_query_rows_hold_nan(D, causal):
+    """The E4M3 NaN code in every padding query row as well as the padding keys
+    and values: those rows come out O = 0, LSE = -inf, valid rows unaffected."""
+    lens = [300, 17, 256, 0, 511]
+    o, lse, o_ref, l_ref = run_fwd(5, 4, 2, 512, 512, D, causal, lens=lens, seed=5 + D, poison=True, poison_q=True)
+    check(o, lse, o_ref, l_ref, f"fp8 NaN query padding D{D} causal{causal}")
 
 
 @pytest.mark.parametrize("scales", [(0.01, 0.02, 0.03), (0.02, -0.015, S0), (S0, S0, -2 * S0)])

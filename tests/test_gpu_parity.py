@@ -53,13 +53,16 @@ def gen(shape, seed, dtype, device="cuda"):
     return torch.randn(shape, generator=g, dtype=torch.float32).to(dtype).to(device)
 
 
-def run_case(B, Hq, Hkv, Tq, Tk, D, dtype, causal, lens=None, scale=None, seed=0, poison=False):
+def run_case(B, Hq, Hkv, Tq, Tk, D, dtype, causal, lens=None, scale=None, seed=0, poison=False, poison_q=False):
     q = gen((B, Hq, Tq, D), seed, dtype)
     k = gen((B, Hkv, Tk, D), seed + 1, dtype)
     v = gen((B, Hkv, Tk, D), seed + 2, dtype)
     if poison and lens is not None:
         workloads.poison_tail_(k, lens)
         workloads.poison_tail_(v, lens)
+    if poison_q and lens is not None:
+        # with Tq == Tk the lengths cover the query rows too: the rest is padding
+        workloads.poison_tail_(q, lens)
     kv = None if lens is None else torch.tensor(lens, dtype=torch.int32, device="cuda")
     sc = 1.0 / math.sqrt(D) if scale is None else scale
     o, lse = ea.fwd(q, k, v, causal=causal, kv_lens=kv, scale=sc)
@@ -164,6 +167,17 @@ def test_bottom_right_causal(dtype, Tq, Tk):
 def test_ragged_with_poison(dtype, causal):
     lens = [1, 0, 700, 129, 64, 65]
     run_case(6, 4, 2, 700, 700, 128, dtype, causal, lens=lens, seed=3, poison=True)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("causal", [False, True])
+def test_padding_query_rows_hold_nan(D, dtype, causal):
+    """Padding query rows (Tq == Tk, rows >= kv_lens[b]) filled with NaN, as
+    are the padding keys and values: those rows come out O = 0, LSE = -inf,
+    and the NaN reaches no valid row; lengths that end inside a wave's rows."""
+    lens = [300, 17, 256, 0, 511]
+    run_case(5, 4, 2, 512, 512, D, dtype, causal, lens=lens, seed=21 + D, poison=True, poison_q=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
