@@ -284,11 +284,15 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // the group's waves.  Each 1 KiB wave-load covers 1024 / (D ESZ) rows;
   // lane l lands at byte 16 l of it, i.e. at (row, slot), and fetches the
   // chunk that the swizzle stores in that slot (the E4M3 V tile is stored
-  // as is: it is only read back row by row for widening).  Rows at or past
-  // Lk are replaced by row Lk-1 (finite data; those keys are masked).  The
-  // row and in-row byte offset of each lane's chunk are fixed per copy slot.
-  constexpr int CPR = D * C::ESZ / 16;   // 16-byte chunks per row
-  int dma_row[C::VMEM_PER_TILE], dma_col[C::VMEM_PER_TILE];
+  // as is: it is only read back row by row for widening).  Each lane's
+  // byte offset from the tile's first row is fixed per copy slot; the
+  // tile's base address is wave-uniform, so a copy is one unsigned min of
+  // that offset against the last chunk of row Lk-1 (rows at or past Lk
+  // read finite data, and those keys are masked) plus the load, addressed
+  // as scalar base + 32-bit lane offset.
+  constexpr int RB = D * C::ESZ;   // bytes per row
+  constexpr int CPR = RB / 16;     // 16-byte chunks per row
+  uint32_t dma_off[C::VMEM_PER_TILE];
 #pragma unroll
   for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
     const int ci = (wg + NWG * i) % (2 * C::LOADS);
@@ -300,17 +304,17 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
       ch = t ? slot : slot ^ swz_k8<D>(r);
     else
       ch = slot ^ (t ? swz_v<D>(r) : swz_k<D>(r));
-    dma_row[i] = r;
-    dma_col[i] = ch * 16;
+    dma_off[i] = (uint32_t)(r * RB + ch * 16);
   }
   auto issue = [&](int lt, int st) {
-    const int kbase = tile_of(lt) * C::BN;
+    // tiles issued past the group's keys (prologue) start at row Lk-1
+    const int kb = min(tile_of(lt) * C::BN, Lk - 1);
+    const uint32_t lim = (uint32_t)(min(Lk - kb, C::BN) * RB - 16);
 #pragma unroll
     for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
       const int ci = (wg + NWG * i) % (2 * C::LOADS);
       const int t = ci / C::LOADS, li = ci - t * C::LOADS;
-      const int key = min(kbase + dma_row[i], Lk - 1);
-      const uint8_t* g = (t ? Vp : Kp) + (size_t)key * D * C::ESZ + dma_col[i];
+      const uint8_t* g = (t ? Vp : Kp) + (size_t)kb * RB + min(dma_off[i], lim);
       __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)(ring8 + (st * 2 + t) * C::TB + li * 1024), 16, 0, 0);
     }
   };
