@@ -74,19 +74,25 @@ __device__ __forceinline__ lds_u16* lds_base(lds_u16* p) {
 
 // HBM -> LDS copy of rows [row0, row0 + ROWS) of a [rows x D] bf16 matrix
 // into a swizzled tile; each of the NWV waves issues PER 1 KiB wave-loads.
-// Rows at or past `last` are replaced by row `last` (finite data; masked).
+// Rows at or past `last` are replaced by the last 16 bytes of row `last`
+// (finite data; masked).  The tile's first row is wave-uniform, so each
+// copy is addressed as that row's address plus the lane's byte offset
+// (fixed per slot), clamped by one unsigned min.
 template <int D, int ROWS, int NWV>
 __device__ __forceinline__ void copy_tile(const u16* src, int row0, int last, u16* dst, int w, int lane) {
   constexpr int LOADS = ROWS * D * 2 / 1024;
   constexpr int PER = (LOADS + NWV - 1) / NWV;
+  const int rb = min(row0, last);
+  const uint32_t lim = (uint32_t)((min(last - rb + 1, ROWS) * D - 8) * 2);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(src + (size_t)rb * D);
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int li = (w + NWV * i) % LOADS;
     const int e = li * 512 + lane * 8;
     const int r = e / D, slot = (e % D) / 8;
     const int ch = slot ^ swz<D>(r);
-    const int row = min(row0 + r, last);
-    __builtin_amdgcn_global_load_lds((gptr_t*)(src + (size_t)row * D + ch * 8), (lptr_t*)(dst + li * 512), 16, 0, 0);
+    const uint32_t off = (uint32_t)((r * D + ch * 8) * 2);
+    __builtin_amdgcn_global_load_lds((gptr_t*)(base + min(off, lim)), (lptr_t*)(dst + li * 512), 16, 0, 0);
   }
 }
 
