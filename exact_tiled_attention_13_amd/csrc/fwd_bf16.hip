@@ -393,14 +393,15 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   auto do_max = [&](f32x16* sd, int kbase) {
     const bool need_mask = kbase + C::BN - 1 > kfull;
     if (need_mask) {
+      // key kbase + 4 h + (32 kb + 8 (r >> 2) + (r & 3)) is allowed up to
+      // lim: compare the constant part against a per-lane bound
       const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
+      const int rel = lim - kbase - 4 * h;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kbase + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          sd[kb][r] = key <= lim ? sd[kb][r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r)
+          sd[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3)) <= rel ? sd[kb][r] : kNegInf;
     }
     float mx = kNegInf;
 #pragma unroll
