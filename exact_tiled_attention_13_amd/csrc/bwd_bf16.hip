@@ -417,8 +417,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     step_rows(sidx, hq, q0);
     const size_t qbase = ((size_t)b * Hq + hq) * (size_t)Tq;
     u16* base = smem + st * STAGE;
-    // rows at or past Lq (padding; may hold anything) are replaced by row
-    // Lq - 1, and the mask below gives them no weight
+    // rows at or past Lq (padding; may hold anything) are replaced by data
+    // of row Lq - 1, and the mask below gives them no weight
     copy_tile<D, BMQ, NW>(Q + qbase * D, q0, Lq - 1, base, w, lane);
     copy_tile<D, BMQ, NW>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
     const int row = min(q0 + r32, Lq - 1);

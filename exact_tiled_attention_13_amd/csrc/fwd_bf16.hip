@@ -484,7 +484,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // ---- main loop.  Every key group runs `per` iterations, so that all
   // waves meet the same barriers; a group with a shorter share idles
   // through its last iteration.  The first NS-1 stages are always filled
-  // (past the group's keys with copies of row Lk-1, never read), so that
+  // (past the group's keys with data of row Lk-1, never read), so that
   // the number of copies in flight here is fixed and the wait for the Q
   // loads above does not also wait for them.
   // (A workgroup with no keys at all, e.g. query rows past a sequence's
