@@ -52,6 +52,9 @@
 namespace miattn {
 namespace {
 
+// lazy-rescale threshold of the running maximum, in log2 units
+constexpr float kDecThresh = 8.0f;
+
 constexpr int kNW = 4;       // waves (= splits) per workgroup
 // keys per tile: bf16, E4M3 (16 KiB of K and V per tile either way)
 template <bool FP8>
@@ -167,7 +170,7 @@ __device__ __forceinline__ bool find_item(int t, const int32_t* __restrict__ kv_
 // the item's page numbers once (one per lane) and every row address takes
 // its page from that vector with a lane shuffle.
 template <int D, bool PAGED, bool FP8>
-__global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
+__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(2))) void decode_split_kernel(
     const void* __restrict__ Qp, const void* __restrict__ Kp, const void* __restrict__ Vp,
     const int32_t* __restrict__ kv_lens, float* __restrict__ ws_o, float* __restrict__ ws_ml,
     int32_t* __restrict__ ws_idx, int B, int Hq, int Hkv, int S_max, int NS, int NHB, float c, int negq,
@@ -397,12 +400,20 @@ __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = xhalf_max(mx);
+    // the reference m moves only when a column's maximum passes it by more
+    // than kDecThresh (log2 units; a wave-uniform test), so P <= 2^8 and the
+    // accumulators are rescaled on few tiles; any reference gives the same
+    // result, and the partial is written with the one it was summed against
     const float mt = (mx == kNegInf) ? kNegInf : mx * c;
-    const float mnew = fmaxf(m, mt);
-    const float muse = (mnew == kNegInf) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
-    m = mnew;
-    const float nm = -muse;
+    if (__builtin_amdgcn_ballot_w64(mt > m + kDecThresh) != 0) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - ((mnew == kNegInf) ? 0.f : mnew));
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float nm = (m == kNegInf) ? 0.f : -m;
     // P^T operands, one per 32 keys: element e of pf[hf] is key
     // 32 hf + 16 (e/4) + 4 g + e%4
     bf16x8 pf[KB / 2];
@@ -416,9 +427,7 @@ __global__ __launch_bounds__(64 * kNW) void decode_split_kernel(
         ps += p;
         pf[kb >> 1][4 * (kb & 1) + r] = static_cast<__bf16>(p);
       }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    lsum += ps;
 
     // the matching V^T fragment: rows 4 g.. and 16 + 4 g.. (of each 32-key
     // half) of column 16 db + j
