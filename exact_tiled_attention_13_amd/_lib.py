@@ -15,7 +15,7 @@ MIATTN_BF16 = 1
 MIATTN_E4M3 = 2
 MIATTN_TILE_FWD = 0
 MIATTN_TILE_DECODE = 1
-MIATTN_TILE_FIELDS = 8
+MIATTN_TILE_FIELDS = 10
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_decode_fp8",
             "attn_decode_paged_fp8", "attn_bwd_workspace_size", "attn_bwd", "attn_set_tile_table",
@@ -65,7 +65,7 @@ def load() -> ctypes.CDLL:
     lib.attn_set_tile_table.restype = i
     lib.attn_tile_table_size.argtypes = []
     lib.attn_tile_table_size.restype = i
-    lib.attn_tile_choice.argtypes = [i, i, i, i, ctypes.c_longlong, vp]
+    lib.attn_tile_choice.argtypes = [i, i, i, i, ctypes.c_longlong, ctypes.c_longlong, vp]
     lib.attn_tile_choice.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -178,10 +178,11 @@ def attn_tile_table_size() -> int:
     return int(load().attn_tile_table_size())
 
 
-def attn_tile_choice(op, dtype, D, causal, size, check=True):
+def attn_tile_choice(op, dtype, D, causal, T, size, check=True):
     """(v0, v1) that a launch with this key uses (see include/miattn.h)."""
     out = (ctypes.c_int32 * 2)()
-    code = load().attn_tile_choice(int(op), int(dtype), int(D), int(causal), int(size), ctypes.cast(out, ctypes.c_void_p))
+    code = load().attn_tile_choice(int(op), int(dtype), int(D), int(causal), int(T), int(size),
+                                   ctypes.cast(out, ctypes.c_void_p))
     if check:
         _check(code)
         return int(out[0]), int(out[1])

@@ -2,6 +2,7 @@
 // error reporting.  Every check runs before any HIP call.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 
@@ -19,6 +20,10 @@ int hip_fail(hipError_t e) {
 
 bool supported_d(int D) { return D == 64 || D == 128; }
 
+// Alignment rules of include/miattn.h (NULL passes: its own check comes first).
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool a4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
 // The scores are scale * (q_scale q).(k_scale k): the product must be finite.
 bool fp8_scales_ok(float scale, float q_scale, float k_scale, float v_scale) {
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale)) return false;
@@ -31,22 +36,24 @@ bool fp8_scales_ok(float scale, float q_scale, float k_scale, float v_scale) {
 namespace miattn {
 
 int device_cu_count() {
-  static int cached[64] = {0};
+  // Per-device cache.  Threads that race on a device's first call all store
+  // the same value; relaxed atomics make that race well defined.
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;  // every thread stores the same value
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 }  // namespace miattn
 
 extern "C" {
 
-int attn_abi_version(void) { return 4; }
+int attn_abi_version(void) { return 5; }
 
 const char* attn_strerror(int code) {
   switch (code) {
@@ -56,6 +63,8 @@ const char* attn_strerror(int code) {
     case MIATTN_ERR_UNSUPPORTED: return "unsupported argument (D must be 64 or 128, dtype 0/1, causal 0/1)";
     case MIATTN_ERR_WORKSPACE: return "workspace missing or smaller than the size the matching *_workspace_size() gives";
     case MIATTN_ERR_HIP: return g_hip_msg;
+    case MIATTN_ERR_ALIGN:
+      return "misaligned pointer (tensors and workspaces need 16-byte alignment; lse, kv_lens and block_table 4)";
     default: return "unknown error code";
   }
 }
@@ -63,6 +72,7 @@ const char* attn_strerror(int code) {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Tq,
              int Tk, int D, float scale, int causal, const int32_t* kv_lens, int dtype, void* stream) {
   if (!q || !k || !v || !o) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || !a4(lse) || !a4(kv_lens)) return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
   if (!supported_d(D) || (dtype != MIATTN_F32 && dtype != MIATTN_BF16) || (causal != 0 && causal != 1))
@@ -79,6 +89,7 @@ int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* ls
                  int Tk, int D, float scale, float q_scale, float k_scale, float v_scale, int causal,
                  const int32_t* kv_lens, void* stream) {
   if (!q || !k || !v || !o) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || !a4(lse) || !a4(kv_lens)) return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale) ||
       !fp8_scales_ok(scale, q_scale, k_scale, v_scale))
     return MIATTN_ERR_SHAPE;
@@ -104,6 +115,7 @@ int decode_common(const void* q, const void* k, const void* v, const int32_t* bl
                   float k_scale, float v_scale, void* stream) {
   const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
   if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+  if (!a16(workspace)) return MIATTN_ERR_ALIGN;
   const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
   if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
   // work items (sequence, head block, split) are counted in int32
@@ -137,6 +149,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, void* workspace,
                 size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k_cache || !v_cache || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k_cache) || !a16(v_cache) || !a16(o) || !a4(lse) || !a4(kv_lens)) return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
   if (!supported_d(D) || (dtype != MIATTN_F32 && dtype != MIATTN_BF16)) return MIATTN_ERR_UNSUPPORTED;
@@ -155,6 +168,7 @@ int attn_decode_fp8(const void* q, const void* k_cache, const void* v_cache, voi
                     int Hkv, int S_max, int D, float scale, float q_scale, float k_scale, float v_scale,
                     const int32_t* kv_lens, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k_cache) || !a16(v_cache) || !a16(o) || !a4(lse) || !a4(kv_lens)) return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale) ||
       !fp8_scales_ok(scale, q_scale, k_scale, v_scale))
     return MIATTN_ERR_SHAPE;
@@ -168,6 +182,8 @@ int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, c
                       float scale, const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype,
                       void* stream) {
   if (!q || !k_pages || !v_pages || !block_table || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k_pages) || !a16(v_pages) || !a16(o) || !a4(lse) || !a4(kv_lens) || !a4(block_table))
+    return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || max_blocks <= 0 || D <= 0 || Hq % Hkv != 0 ||
       !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
@@ -184,6 +200,8 @@ int attn_decode_paged_fp8(const void* q, const void* k_pages, const void* v_page
                           int D, float scale, float q_scale, float k_scale, float v_scale, const int32_t* kv_lens,
                           void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_pages || !v_pages || !block_table || !o || !kv_lens) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k_pages) || !a16(v_pages) || !a16(o) || !a4(lse) || !a4(kv_lens) || !a4(block_table))
+    return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || max_blocks <= 0 || D <= 0 || Hq % Hkv != 0 ||
       !std::isfinite(scale) || !fp8_scales_ok(scale, q_scale, k_scale, v_scale))
     return MIATTN_ERR_SHAPE;
@@ -204,6 +222,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Tq, int Tk, int D, float scale, int causal,
              const int32_t* kv_lens, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return MIATTN_ERR_NULL;
+  if (!a16(q) || !a16(k) || !a16(v) || !a16(o) || !a4(lse) || !a16(dout) || !a16(dq) || !a16(dk) || !a16(dv) ||
+      !a4(kv_lens))
+    return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
   if (!supported_d(D) || dtype != MIATTN_BF16 || (causal != 0 && causal != 1)) return MIATTN_ERR_UNSUPPORTED;
@@ -213,6 +234,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
     return MIATTN_ERR_SHAPE;
   const size_t need = attn_bwd_workspace_size(B, Hq, Tq);
   if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
+  if (!a16(workspace)) return MIATTN_ERR_ALIGN;
   miattn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, kv_lens, B, Hq, Hkv, Tq, Tk, D, scale, causal,
                     static_cast<float*>(workspace)};
   hipError_t e = miattn::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));

@@ -570,7 +570,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
   // workgroups per CU from the launch table (built-in: two, i.e. 8 waves),
   // never more waves than work items
   const long long items = (long long)a.B * NS * a.Hkv * NHB;
-  const long long per_cu = choose_decode_wgs_per_cu(FP8 ? MIATTN_E4M3 : MIATTN_BF16, D, items);
+  const long long per_cu = choose_decode_wgs_per_cu(FP8 ? MIATTN_E4M3 : MIATTN_BF16, D, a.S_max, items);
   const long long wgs = std::min<long long>(per_cu * device_cu_count(), (items + kNW - 1) / kNW);
   const int nwav = (int)wgs * kNW;
   hipLaunchKernelGGL((decode_split_kernel<D, PAGED, FP8>), dim3((unsigned)wgs), dim3(64 * kNW), 0, st, a.q,

@@ -696,7 +696,7 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t st) {
   // doubles the number of workgroups.  That is the built-in rule; the
   // launch table may choose otherwise per size bucket.
   const long long wg256 = (long long)((a.Tq + 255) / 256) * a.B * a.Hq;
-  const FwdChoice ch = choose_fwd(FP8 ? MIATTN_E4M3 : MIATTN_BF16, D, CAUSAL ? 1 : 0, wg256);
+  const FwdChoice ch = choose_fwd(FP8 ? MIATTN_E4M3 : MIATTN_BF16, D, CAUSAL ? 1 : 0, a.Tk, wg256);
   if (ch.shape == 0) return launch<D, 8, 1, CAUSAL, FP8>(a, st, ch.zig);
   return launch<D, 4, 2, CAUSAL, FP8>(a, st, ch.zig);
 }

@@ -85,14 +85,16 @@ int device_cu_count();
 
 // Launch choices (tiles.cpp).  Prefill: shape 0 = 256-row workgroups with
 // one key group, 1 = 128-row workgroups with two key groups; zig 0/1, or -1
-// for the built-in rule.  wg256 = ceil(Tq / 256) * B * Hq.
+// for the built-in rule.  T = Tk (keys per sequence),
+// wg256 = ceil(Tq / 256) * B * Hq.
 struct FwdChoice {
   int shape, zig;
 };
 constexpr long long kFwdSplitBelow = 512;
-FwdChoice choose_fwd(int dtype, int D, int causal, long long wg256);
-// Decode: split-kernel workgroups per CU for items = B * NS * Hkv * ceil(G / 16).
-int choose_decode_wgs_per_cu(int dtype, int D, long long items);
+FwdChoice choose_fwd(int dtype, int D, int causal, long long T, long long wg256);
+// Decode: split-kernel workgroups per CU, keyed by S_max and the work-item
+// count items = B * NS * Hkv * ceil(G / 16).
+int choose_decode_wgs_per_cu(int dtype, int D, long long S_max, long long items);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t st);

@@ -46,6 +46,12 @@
  * on `stream` (a hipStream_t; NULL = the default stream); calls return as
  * soon as the work is queued.  Functions are thread-safe.
  *
+ * Alignment.  The kernels move tensors in 16-byte pieces: q, k, v, o, the
+ * caches and page pools, dout, dq, dk, dv and every workspace must start on
+ * a 16-byte boundary; lse, kv_lens and block_table on a 4-byte boundary
+ * (else MIATTN_ERR_ALIGN).  Allocations from hipMalloc (and PyTorch) always
+ * are; a view at a storage offset may not be.
+ *
  * Errors.  Return 0 on success or a negative MIATTN_ERR_* code.  Arguments
  * are checked before any HIP call; a failed check launches nothing.  Errors
  * never abort the process.
@@ -72,7 +78,8 @@ enum {
   MIATTN_ERR_SHAPE = -2,       /* size <= 0, Hq % Hkv != 0, non-finite scale(s), or grid too large */
   MIATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, causal not 0/1 */
   MIATTN_ERR_WORKSPACE = -4,   /* workspace missing or too small */
-  MIATTN_ERR_HIP = -5          /* the HIP runtime refused a launch; see attn_strerror */
+  MIATTN_ERR_HIP = -5,         /* the HIP runtime refused a launch; see attn_strerror */
+  MIATTN_ERR_ALIGN = -6        /* a pointer is not aligned as required (see Alignment above) */
 };
 
 /*
@@ -213,34 +220,39 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 /*
  * Launch-choice table.  The NumPy tiled-attention build guide, section
  * Extending It, suggests picking the tile configuration per head size and
- * hardware by measurement and persisting the result; here the compiled
- * kernels take their launch shape as a runtime choice, looked up in this
- * table (the Python binding fills it from the JSON file its tuner writes).
- * Keys not covered, or no table, use the built-in rule.  Every choice gives
- * a correct result; only speed differs.
+ * hardware by measurement, adapting it to varying sequence lengths, and
+ * persisting the result; here the compiled kernels take their launch shape
+ * as a runtime choice, looked up in this table (the Python binding fills it
+ * from the JSON file its tuner writes).  Keys not covered, or no table, use
+ * the built-in rule.  Every choice gives a correct result; only speed
+ * differs.
  *
  * An entry is MIATTN_TILE_FIELDS int32:
- *   { op, dtype, D, causal, size_lo, size_hi, v0, v1 }
+ *   { op, dtype, D, causal, t_lo, t_hi, size_lo, size_hi, v0, v1 }
  *   op    MIATTN_TILE_FWD: attn_fwd (dtype MIATTN_BF16) and attn_fwd_fp8
- *         (MIATTN_E4M3); size = ceil(Tq / 256) * B * Hq; v0 = 0 for
+ *         (MIATTN_E4M3); T = Tk; size = ceil(Tq / 256) * B * Hq; v0 = 0 for
  *         256-row workgroups with one key group, 1 for 128-row workgroups
  *         whose two key groups split the keys; v1 = 1 to pair causal query
  *         tiles long with short, 0 not to, -1 for the built-in rule.
  *   op    MIATTN_TILE_DECODE: the bf16 and E4M3 decode calls, causal = 1;
+ *         T = S_max (max_blocks * page_size for the paged calls);
  *         size = B * ceil(S_max / 512) * Hkv * ceil(Hq / Hkv / 16);
  *         v0 = workgroups of the split kernel per compute unit (1..8),
  *         v1 = 0.
- * The first entry whose key matches (size_lo <= size <= size_hi) wins.
- * attn_set_tile_table copies n entries (n <= 256; n = 0 clears the table)
- * and returns MIATTN_ERR_UNSUPPORTED for an invalid entry, leaving the old
- * table in place.  It is thread-safe; calls running concurrently see the
- * old or the new table.  attn_tile_choice writes the (v0, v1) a launch with
- * that key would use (v1 = -1: the built-in zig-zag rule).
+ * The first entry whose key matches (t_lo <= T <= t_hi and
+ * size_lo <= size <= size_hi) wins.  attn_set_tile_table copies n entries
+ * (n <= 256; n = 0 clears the table) and returns MIATTN_ERR_UNSUPPORTED for
+ * an invalid entry, leaving the old table in place.  Launches read the table
+ * without locking: each call of attn_set_tile_table publishes a new
+ * immutable copy, so launches running concurrently see the old or the new
+ * table, never a mix; earlier copies stay allocated until the process ends.
+ * attn_tile_choice writes the (v0, v1) a launch with that key would use
+ * (v1 = -1: the built-in zig-zag rule).
  */
-enum { MIATTN_TILE_FWD = 0, MIATTN_TILE_DECODE = 1, MIATTN_TILE_FIELDS = 8 };
+enum { MIATTN_TILE_FWD = 0, MIATTN_TILE_DECODE = 1, MIATTN_TILE_FIELDS = 10 };
 int attn_set_tile_table(const int32_t* entries, int n);
 int attn_tile_table_size(void);
-int attn_tile_choice(int op, int dtype, int D, int causal, long long size, int32_t* out);
+int attn_tile_choice(int op, int dtype, int D, int causal, long long T, long long size, int32_t* out);
 
 /* Static text for a return code; for MIATTN_ERR_HIP, the last HIP error seen
  * by the calling thread. */

@@ -126,11 +126,14 @@ def attention(q, k, v, scale: float, causal: bool = False, kv_lens=None, row_chu
     return o, lse
 
 
-def attention_rows(q, k, v, rows, scale: float, causal: bool = False, kv_lens=None):
+def attention_rows(q, k, v, rows, scale: float, causal: bool = False, kv_lens=None, row_chunk: int = 256):
     """The same definition, evaluated only at the listed (b, h, i) rows.
 
-    ``rows`` is an iterable of (b, h, i).  Only the touched K/V heads are
-    upcast, so this reaches full-size inputs (e.g. a 32k causal prefill).
+    ``rows`` is an iterable of (b, h, i).  Rows of one (b, h) are evaluated
+    together, ``row_chunk`` at a time, each against every key it may see (the
+    plain softmax over the full row, as in ``attention``); only the touched
+    query rows and K/V heads are upcast, so this reaches full-size inputs
+    (e.g. a 32k causal prefill).
     Returns (o (n, D) float64, lse (n,) float64) in the order of ``rows``.
     """
     rows = [tuple(int(x) for x in r) for r in rows]
@@ -140,21 +143,27 @@ def attention_rows(q, k, v, rows, scale: float, causal: bool = False, kv_lens=No
     lk_all, lq_all = valid_lengths(B, Tq, Tk, kv_lens)
     o = np.zeros((len(rows), D), dtype=np.float64)
     lse = np.full((len(rows),), -np.inf, dtype=np.float64)
-    cache = {}
+    groups = {}
     for n, (b, h, i) in enumerate(rows):
+        if i < lq_all[b]:
+            groups.setdefault((b, h), []).append((i, n))
+    kv_cache = {}
+    for (b, h), members in sorted(groups.items()):
         lk, lq = lk_all[b], lq_all[b]
-        if i >= lq:
-            continue
         hk = h // G
-        if (b, hk) not in cache:
-            if len(cache) > 4:
-                cache.clear()
-            cache[(b, hk)] = (_as_f64(k[b, hk, :lk]), _as_f64(v[b, hk, :lk]))
-        kk, vv = cache[(b, hk)]
-        qi = _as_f64(q[b, h, i : i + 1])
-        ob, lb = _rows_block(qi, kk, vv, scale, np.array([i]), lk, lk - lq, causal)
-        o[n] = ob[0]
-        lse[n] = lb[0]
+        if (b, hk) not in kv_cache:
+            kv_cache.clear()
+            kv_cache[(b, hk)] = (_as_f64(k[b, hk, :lk]), _as_f64(v[b, hk, :lk]))
+        kk, vv = kv_cache[(b, hk)]
+        members.sort()
+        for c0 in range(0, len(members), row_chunk):
+            part = members[c0:c0 + row_chunk]
+            idx = np.array([i for i, _ in part], dtype=np.int64)
+            qi = np.stack([_as_f64(q[b, h, i]) for i in idx.tolist()])
+            ob, lb = _rows_block(qi, kk, vv, scale, idx, lk, lk - lq, causal)
+            for r, (_, n) in enumerate(part):
+                o[n] = ob[r]
+                lse[n] = lb[r]
     return o, lse
 
 

@@ -98,27 +98,95 @@ def attention_backward(q, k, v, do, scale, causal=False, kv_lens=None, row_chunk
     return dq, dk, dv
 
 
-def backward_rows(q, k, v, do, rows, scale, causal=False, kv_lens=None):
+def backward_rows(q, k, v, do, rows, scale, causal=False, kv_lens=None, row_chunk=256):
     """dQ of selected (b, h, i) rows only (float64, shape (len(rows), D)).
 
     A row's dQ needs only that row's softmax, so this reaches sizes where the
-    full backward is too slow on the CPU."""
+    full backward is too slow on the CPU.  Rows of one (b, h) are evaluated
+    together, ``row_chunk`` at a time, each against every key it sees."""
+    rows = [tuple(int(x) for x in r) for r in rows]
     B, Hq, Tq, D = q.shape
     Hkv, Tk = k.shape[1], k.shape[2]
     G = Hq // Hkv
     lk_all, lq_all = valid_lengths(B, Tq, Tk, kv_lens)
     out = np.zeros((len(rows), D), dtype=np.float64)
+    groups = {}
     for n, (b, h, i) in enumerate(rows):
+        if i < lq_all[b] and lk_all[b] > 0:
+            groups.setdefault((b, h), []).append((i, n))
+    for (b, h), members in sorted(groups.items()):
         lk, lq = lk_all[b], lq_all[b]
-        if i >= lq or lk <= 0:
-            continue
         hk = h // G
         kk = _as_f64(k[b, hk, :lk])
         vv = _as_f64(v[b, hk, :lk])
-        qi = _as_f64(q[b, h, i:i + 1])
-        g = _as_f64(do[b, h, i:i + 1])
-        p = _weights(qi, kk, scale, np.array([i]), lk, lk - lq, causal)
-        dp = g @ vv.T
-        ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
-        out[n] = scale * (ds @ kk)[0]
+        members.sort()
+        for c0 in range(0, len(members), row_chunk):
+            part = members[c0:c0 + row_chunk]
+            idx = np.array([i for i, _ in part], dtype=np.int64)
+            qi = np.stack([_as_f64(q[b, h, i]) for i in idx.tolist()])
+            g = np.stack([_as_f64(do[b, h, i]) for i in idx.tolist()])
+            p = _weights(qi, kk, scale, idx, lk, lk - lq, causal)
+            dp = g @ vv.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq = scale * (ds @ kk)
+            for r, (_, n) in enumerate(part):
+                out[n] = dq[r]
     return out
+
+
+def backward_key_rows(q, k, v, do, o, lse, keys, scale, causal=False, kv_lens=None):
+    """dK and dV of selected keys (b, hk, j) only (float64, each (len(keys), D)).
+
+    The Interview question's Task 2 / Hint 2 recomputes the weights from the
+    inputs and the forward's saved per-row statistics; this does the same
+    for a set of keys: with the forward's output o and natural-log row
+    statistic lse given, P_ij = exp(scale q_i . k_j - lse_i) and
+    Drow_i = sum_d dO_id O_id for every query row i of the KV head's query
+    heads that sees key j, then
+
+        dV_j = sum_i P_ij dO_i,   dK_j = scale sum_i P_ij (dO_i . v_j - Drow_i) q_i,
+
+    summed over the query heads sharing the KV head.  Rows that are padding
+    or have lse = -inf contribute nothing; keys at or past a sequence's
+    length get zeros.  A key's gradient needs only the rows that see it, so
+    this reaches sizes where ``attention_backward`` is too slow.
+    """
+    keys = [tuple(int(x) for x in r) for r in keys]
+    B, Hq, Tq, D = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    lk_all, lq_all = valid_lengths(B, Tq, Tk, kv_lens)
+    dk = np.zeros((len(keys), D), dtype=np.float64)
+    dv = np.zeros((len(keys), D), dtype=np.float64)
+    groups = {}
+    for n, (b, hk, j) in enumerate(keys):
+        if j < lk_all[b]:
+            groups.setdefault((b, hk), []).append((j, n))
+    for (b, hk), members in sorted(groups.items()):
+        lk, lq = lk_all[b], lq_all[b]
+        off = lk - lq
+        js = np.array([j for j, _ in members], dtype=np.int64)
+        kj = _as_f64(k[b, hk])[js]                     # (m, D)
+        vj = _as_f64(v[b, hk])[js]
+        gk = np.zeros_like(kj)
+        gv = np.zeros_like(vj)
+        i = np.arange(lq)
+        for h in range(hk * G, (hk + 1) * G):
+            qh = _as_f64(q[b, h, :lq])                 # (lq, D)
+            gh = _as_f64(do[b, h, :lq])
+            oh = _as_f64(o[b, h, :lq])
+            lh = _as_f64(lse[b, h, :lq]).reshape(-1)
+            seen = np.isfinite(lh)[:, None] & np.ones((lq, len(js)), dtype=bool)
+            if causal:
+                seen &= js[None, :] <= (i[:, None] + off)
+            s = scale * (qh @ kj.T)                    # (lq, m)
+            p = np.where(seen, np.exp(np.where(seen, s - np.where(np.isfinite(lh), lh, 0.0)[:, None], 0.0)), 0.0)
+            drow = (gh * oh).sum(axis=1, keepdims=True)
+            dp = gh @ vj.T
+            ds = p * (dp - drow)
+            gv += p.T @ gh
+            gk += scale * (ds.T @ qh)
+        for r, (_, n) in enumerate(members):
+            dk[n] = gk[r]
+            dv[n] = gv[r]
+    return dk, dv

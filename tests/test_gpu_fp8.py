@@ -206,21 +206,31 @@ def test_fp8_prefill_full_size_causal():
     check(o, lse, o_ref, l_ref, "fp8 causal full size")
 
 
-def test_fp8_prefill_long_sampled():
-    """The E4M3 long-context workload (T=32768) on sampled rows, first and last included."""
+def test_fp8_prefill_long_two_heads_and_random_rows():
+    """The E4M3 long-context workload (B1 H32 T32768 D128) at full size: all
+    rows of heads 0 and 31 against the dense oracle, plus 4096 random rows
+    of the other heads against the row oracle."""
     w = workloads.WORKLOADS["long-fp8"]
     inp = workloads.make("long-fp8", seed=0)
     sc = inp["fp8_scales"]
     o, lse = ea.fwd_fp8(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), q_scale=sc[0], k_scale=sc[1],
                         v_scale=sc[2], causal=True)
     torch.cuda.synchronize()
+    heads = (0, w.Hq - 1)
+    for h in heads:
+        sl = slice(h, h + 1)
+        o_ref, l_ref = oracle.attention_fp8(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], *sc, w.scale,
+                                            causal=True)
+        check(o[:, sl], lse[:, sl], o_ref, l_ref, f"fp8 long head {h}, all {w.Tq} rows")
     rng = np.random.default_rng(1)
-    rows = [(0, 0, 0), (0, 31, w.Tq - 1), (0, 5, 255), (0, 6, 256)]
-    rows += [(0, int(h), int(i)) for h, i in zip(rng.integers(0, w.Hq, 12), rng.integers(0, w.Tq, 12))]
+    others = [h for h in range(w.Hq) if h not in heads]
+    picked = set()
+    while len(picked) < 4096:
+        picked.add((int(rng.choice(others)), int(rng.integers(w.Tq))))
+    rows = sorted((0, h, i) for h, i in picked)
     o_ref, l_ref = oracle.attention_rows_fp8(inp["q"], inp["k"], inp["v"], rows, *sc, w.scale, causal=True)
-    og = torch.stack([o[0, h, i] for _, h, i in rows])
-    lg = torch.stack([lse[0, h, i] for _, h, i in rows])
-    check(og, lg, o_ref, l_ref, "fp8 long sampled rows")
+    idx = tuple(torch.as_tensor(a, device="cuda") for a in np.array(rows).T)
+    check(o[idx], lse[idx], o_ref, l_ref, f"fp8 long, {len(rows)} random rows of other heads")
 
 
 def test_fp8_prefill_matches_bf16_path_on_exact_values():

@@ -123,3 +123,40 @@ def test_rows_helper_matches_full():
     got = oracle.backward_rows(q, k, v, do, rows, 0.25, True, lens)
     for n, (b, h, i) in enumerate(rows):
         assert np.allclose(got[n], dq[b, h, i], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape,lens", [((2, 4, 2, 37, 37, 8), None), ((3, 4, 1, 21, 21, 5), [21, 0, 9]),
+                                        ((2, 2, 2, 7, 30, 6), None), ((2, 2, 1, 30, 7, 6), [5, 7])])
+def test_key_rows_equal_full_backward(causal, shape, lens):
+    """dK, dV of selected keys from the saved statistics (o, lse of the
+    forward oracle) equal the full backward oracle's, which finite
+    differences and autograd pin above; every key of every KV head,
+    including keys past a length (zeros) and Tq != Tk (bottom-right)."""
+    B, Hq, Hkv, Tq, Tk, D = shape
+    q, k, v, do = rnd((B, Hq, Tq, D), 11), rnd((B, Hkv, Tk, D), 12), rnd((B, Hkv, Tk, D), 13), rnd((B, Hq, Tq, D), 14)
+    sc = 0.45
+    o, lse = oracle.attention(q, k, v, sc, causal, lens)
+    _, dk, dv = oracle.attention_backward(q, k, v, do, sc, causal, lens)
+    keys = [(b, h, j) for b in range(B) for h in range(Hkv) for j in range(Tk)]
+    gk, gv = oracle.backward_key_rows(q, k, v, do, o, lse, keys, sc, causal, lens)
+    ref_k = np.stack([dk[b, h, j] for b, h, j in keys])
+    ref_v = np.stack([dv[b, h, j] for b, h, j in keys])
+    assert np.abs(gk - ref_k).max() <= 1e-10 * max(1.0, np.abs(ref_k).max())
+    assert np.abs(gv - ref_v).max() <= 1e-10 * max(1.0, np.abs(ref_v).max())
+    # a scrambled key order returns the same rows
+    perm = np.random.default_rng(0).permutation(len(keys))
+    pk, pv = oracle.backward_key_rows(q, k, v, do, o, lse, [keys[i] for i in perm], sc, causal, lens)
+    assert np.array_equal(pk, gk[perm]) and np.array_equal(pv, gv[perm])
+
+
+def test_key_rows_use_the_given_statistics():
+    """A planted mistake in the statistics shows: shifting lse by c scales
+    every weight by exp(-c), so dV (linear in P) scales by exp(-c)."""
+    B, Hq, Hkv, T, D = 1, 2, 1, 9, 4
+    q, k, v, do = rnd((B, Hq, T, D), 21), rnd((B, Hkv, T, D), 22), rnd((B, Hkv, T, D), 23), rnd((B, Hq, T, D), 24)
+    o, lse = oracle.attention(q, k, v, 0.5, True)
+    keys = [(0, 0, j) for j in range(T)]
+    _, gv = oracle.backward_key_rows(q, k, v, do, o, lse, keys, 0.5, True)
+    _, gv2 = oracle.backward_key_rows(q, k, v, do, o, lse + 0.3, keys, 0.5, True)
+    assert np.allclose(gv2, gv * math.exp(-0.3), rtol=1e-12, atol=1e-14)
