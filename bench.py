@@ -2,25 +2,34 @@
 """Throughput of the exact-attention hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
-                    [--workload causal|long|ragged|decode|decode-paged|decode-fp8|causal-fp8|long-fp8|single]
-                    [--backward]
+                    [--workload long|causal|ragged|decode|decode-paged|decode-fp8|causal-fp8|long-fp8|single]
+                    [--backward] [--only]
 
 A step is one pass of the hot path over one batch of synthetic, seeded input
-already resident in HBM.  The headline line measures the causal prefill
-workload (B=4, H=16, T=1024, D=64, bf16) in TFLOP/s of algorithmic work
-(4*D flops per unmasked (query, key) pair); the same run also times one
-KV-cache decode step of the GQA decode workload (B=64, Hq=32, Hkv=8, D=128,
-lengths 1024..32768) in GB/s of algorithmic bytes (the K/V rows each sequence
-needs plus q, o, lse and lengths), reported under "decode", the same step on
-E4M3 (FP8) q and caches under "decode_fp8", the causal prefill on E4M3 Q, K,
-V under "prefill_fp8", and the gradients
-of the causal workload (10*D flops per unmasked pair: the five products of
-the backward), reported under "backward".  Steps are
-replayed from a HIP graph (a fixed number of calls per graph) so that host
-launch overhead does not enter the timing; the kernels are timed with HIP
-events recorded on the stream they run on.
+already resident in HBM.  The headline line is the long-context causal
+prefill (B=1, H=32, T=32768, D=128, bf16), the largest prefill configuration,
+in TFLOP/s of algorithmic work (4*D flops per unmasked (query, key) pair).
+The same run measures, as extra keys of the line, each with its own roofline,
+CPU baseline and max-abs errors against the float64 oracle on sampled rows:
 
-The float64 CPU oracle is timed on a bounded sample of the same workload
+  causal        causal prefill B=4 H=16 T=1024 D=64 bf16
+  ragged        ragged key-padding prefill B=8 H=16 T=4096 D=128 bf16
+  decode        KV-cache decode step, GQA B=64 Hq=32 Hkv=8 D=128, lengths
+                1024..32768, in GB/s of algorithmic bytes (the K/V rows each
+                sequence needs plus q, o, lse and lengths)
+  decode_fp8    the same step on E4M3 q and caches
+  prefill_fp8   the long causal prefill on E4M3 Q, K, V
+  backward      gradients of the causal prefill (10*D flops per unmasked
+                pair: the five products of the backward)
+  single        the fp32 single-head workload (latency-bound; information)
+
+Steps are replayed from HIP graphs so that host launch overhead does not
+enter the timing.  `value` is the step's algorithmic work over `ms_per_step`,
+the wall-clock time of exactly K steps between two device synchronisations;
+`roofline.achieved` is the same work over the kernel time measured with HIP
+events recorded on the stream the kernels run on (`roofline.kernel_ms`).
+
+The float64 CPU oracle is timed on a bounded sample of each workload
 (cpu_baseline).  It is a reported baseline, not the target.
 
 roofline.traffic (HBM bytes per launch) and roofline.mfma_busy (share of the
@@ -52,6 +61,9 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
 # kernel name (as rocprofv3 reports it, substring) -> sources it is built from
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h", "launch.h"],
+    "bwd_prep_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
+    "bwd_dq_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
+    "bwd_dkdv_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
     "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
     "decode_split_kernel": ["decode.hip", "device_common.h", "launch.h"],
 }
@@ -104,10 +116,11 @@ def blas_threads():
 
 
 class Graphed:
-    """A HIP graph holding CALLS_PER_GRAPH calls of fn, replayed to run steps."""
+    """A HIP graph holding `calls` calls of fn, replayed to run steps."""
 
-    def __init__(self, torch, fn):
+    def __init__(self, torch, fn, calls=CALLS_PER_GRAPH):
         self.torch = torch
+        self.calls = calls
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -116,26 +129,34 @@ class Graphed:
         torch.cuda.synchronize()
         self.g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.g):
-            for _ in range(CALLS_PER_GRAPH):
+            for _ in range(calls):
                 fn()
         torch.cuda.synchronize()
 
     def run(self, steps):
-        for _ in range(max(1, steps // CALLS_PER_GRAPH)):
+        """Replay whole graphs covering `steps` steps (at least one graph)."""
+        for _ in range(max(1, -(-steps // self.calls))):
             self.g.replay()
 
 
-def time_steps(torch, runner, steps, warmup):
-    """Warm up, then time exactly `steps` steps (rounded to whole graphs)."""
-    runner.run(warmup)
+def time_steps(torch, runner, steps, warmup, fn):
+    """`warmup` untimed eager calls, then exactly the steps of whole graph
+    replays (a multiple of runner.calls, at least `steps`), bracketed by
+    device synchronisations.  Returns (event ms per step, wall ms per step,
+    steps timed): HIP events recorded on the current stream, which the
+    graphs replay on, and the host clock around the synchronised region."""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
-    n = max(1, steps // CALLS_PER_GRAPH) * CALLS_PER_GRAPH
+    reps = max(1, -(-steps // runner.calls))
+    n = reps * runner.calls
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
-    runner.run(n)
+    for _ in range(reps):
+        runner.g.replay()
     ev1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
@@ -179,7 +200,12 @@ def setup_prefill(torch, name):
 
 def setup_backward(torch, name):
     """Gradients of a prefill workload: q, k, v of the workload, a seeded dO,
-    and O, LSE from one forward call."""
+    and O, LSE of the forward.  The (batch, KV head) groups the error report
+    checks get O and LSE from the float64 oracle (rounded as attn_fwd stores
+    them), so that no input of that check comes from the HIP path; other
+    heads, whose gradients are independent of them, take one attn_fwd call."""
+    import oracle
+
     import exact_tiled_attention_13_amd as ea
     from exact_tiled_attention_13_amd import workloads
 
@@ -189,9 +215,23 @@ def setup_backward(torch, name):
         raise SystemExit("the backward pass is bf16 only")
     q, k, v = (w[x].cuda() for x in ("q", "k", "v"))
     g = torch.Generator().manual_seed(1)
-    do = workloads.randn_bf16(tuple(q.shape), g).cuda()
+    do_cpu = workloads.randn_bf16(tuple(w["q"].shape), g)
+    do = do_cpu.cuda()
     kv = None if w["kv_lens"] is None else w["kv_lens"].cuda()
     o, lse = ea.fwd(q, k, v, causal=W.causal, kv_lens=kv, scale=W.scale)
+    G = W.Hq // W.Hkv
+    groups = [(b, hk) for b in range(W.B) for hk in range(W.Hkv)]
+    if W.B * W.Hq > 64:
+        groups = [(0, 0), (W.B - 1, W.Hkv - 1)]
+    o_ref = {}
+    for b, hk in groups:
+        hs = slice(hk * G, (hk + 1) * G)
+        lb = None if w["lens"] is None else w["lens"][b:b + 1]
+        ob, lbse = oracle.attention(w["q"][b:b + 1, hs], w["k"][b:b + 1, hk:hk + 1], w["v"][b:b + 1, hk:hk + 1],
+                                    W.scale, W.causal, lb)
+        o_ref[(b, hk)] = (ob[0], lbse[0])
+        o[b, hs] = torch.from_numpy(ob[0]).to(torch.bfloat16).cuda()
+        lse[b, hs] = torch.from_numpy(lbse[0]).to(torch.float32).cuda()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     nbytes = ea.attn_bwd_workspace_size(W.B, W.Hq, W.Tq)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -204,7 +244,61 @@ def setup_backward(torch, name):
 
     pairs = prefill_pairs(W.B, W.Hq, W.Tq, W.Tk, W.causal, w["lens"])
     return dict(w=w, W=W, step=step, flops=10 * W.D * pairs, keep=(q, k, v, do, kv, o, lse, ws),
-                out=(dq, dk, dv))
+                out=(dq, dk, dv), do_cpu=do_cpu, groups=groups, o_ref=o_ref)
+
+
+def backward_errors(bw, n_rows):
+    """dQ of sampled rows and dK, dV of sampled keys of the oracle-fed
+    (batch, KV head) groups, against the row and key oracles; the bar is
+    max|g - g_ref| <= 2e-2 max|g_ref| per tensor."""
+    import oracle
+    import torch
+
+    w, W = bw["w"], bw["W"]
+    dq, dk, dv = bw["out"]
+    G = W.Hq // W.Hkv
+    rng = np.random.default_rng(4)
+    lk, lq = oracle.valid_lengths(W.B, W.Tq, W.Tk, w["lens"])
+    rows, keys = set(), set()
+    per = max(1, n_rows // len(bw["groups"]))
+    for b, hk in bw["groups"]:
+        for _ in range(per):
+            if lq[b] > 0:
+                rows.add((b, hk * G + int(rng.integers(G)), int(rng.integers(lq[b]))))
+            if lk[b] > 0:
+                keys.add((b, hk, int(rng.integers(lk[b]))))
+    rows, keys = sorted(rows), sorted(keys)
+    o = np.zeros(tuple(w["q"].shape))
+    lse = np.full(tuple(w["q"].shape[:3]), -np.inf)
+    for (b, hk), (ob, lb) in bw["o_ref"].items():
+        o[b, hk * G:(hk + 1) * G], lse[b, hk * G:(hk + 1) * G] = ob, lb
+    q, k, v, do = w["q"], w["k"], w["v"], bw["do_cpu"]
+    ref_q = oracle.backward_rows(q, k, v, do, rows, W.scale, W.causal, w["lens"])
+    ref_k, ref_v = oracle.backward_key_rows(q, k, v, do, o, lse, keys, W.scale, W.causal, w["lens"])
+    out = dict(checked=f"{len(rows)} dQ rows, {len(keys)} dK/dV keys of (batch, KV head) groups {bw['groups'][:4]}"
+                       f"{'...' if len(bw['groups']) > 4 else ''}", rel_tol=2e-2)
+    ok = True
+    for nm, g, idx, ref in (("dq", dq, rows, ref_q), ("dk", dk, keys, ref_k), ("dv", dv, keys, ref_v)):
+        got = g[tuple(torch.as_tensor(a, device=g.device) for a in np.array(idx).T)].float().cpu().double().numpy()
+        err = float(np.abs(got - ref).max())
+        scale = float(np.abs(ref).max())
+        out[f"max_abs_{nm}"] = err
+        out[f"max_ref_{nm}"] = scale
+        ok = ok and np.isfinite(got).all() and err <= 2e-2 * scale + 1e-6
+    out["within_tolerance"] = bool(ok)
+    return out
+
+
+def backward_traffic(workload):
+    """Scaled HBM bytes per step of the three gradient kernels from the
+    committed counter summary, or None (see traffic_for)."""
+    total = 0.0
+    for kn in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"):
+        t = traffic_for(kn, workload)
+        if t is None:
+            return None
+        total += t
+    return total
 
 
 def cpu_baseline_backward(name, budget_s):
@@ -528,21 +622,172 @@ def summarize_pmc(kernel, workload, fetch_dir, write_dir, copy_fetch_dir, copy_w
     print(json.dumps(entry, indent=1))
 
 
+CONTEXT = ("The pages publish no throughput for this path; FlashAttention is said to run 2x-4x faster than "
+           "naive attention kernels (Transformers in Action, section 9.4.1; hardware not stated).")
+TOL = {"bf16": (2e-2, 1e-3), "e4m3": (2e-2, 1e-3), "f32": (1e-4, 1e-3)}
+
+
+def sampled_rows(B, H, T, lens_q, n, seed):
+    """Rows for the error report: first, last and tile-edge rows of every
+    sequence (one random head each), one padding row where there is one,
+    and random valid rows up to n."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in range(B):
+        lq = int(lens_q[b])
+        for i in (0, 127, 128, lq - 1, lq):
+            if 0 <= i < T:
+                rows.add((b, int(rng.integers(H)), i))
+    tries = 0
+    while len(rows) < n and tries < 100 * n:
+        b = int(rng.integers(B))
+        if lens_q[b] > 0:
+            rows.add((b, int(rng.integers(H)), int(rng.integers(lens_q[b]))))
+        tries += 1
+    return sorted(rows)
+
+
+def _errors(o_gpu, l_gpu, o_ref, l_ref, tol, what):
+    o = o_gpu.float().cpu().double().numpy()
+    lg = l_gpu.float().cpu().double().numpy()
+    fin = np.isfinite(l_ref)
+    eo = float(np.abs(o - o_ref).max()) if o.size else 0.0
+    el = float(np.abs(lg[fin] - l_ref[fin]).max()) if fin.any() else 0.0
+    inf_ok = bool(np.array_equal(np.isneginf(lg), np.isneginf(l_ref)))
+    return dict(checked=what, max_abs_o=eo, max_abs_lse=el, neg_inf_lse_match=inf_ok, tol_o=tol[0], tol_lse=tol[1],
+                within_tolerance=bool(eo <= tol[0] and el <= tol[1] and inf_ok and np.isfinite(o).all()))
+
+
+def prefill_errors(pre, n_rows):
+    """Max-abs O and LSE errors of the last replay's outputs against the
+    float64 oracle on sampled rows (the row oracle: only those rows)."""
+    import oracle
+
+    w, W = pre["w"], pre["W"]
+    o, lse = pre["out"]
+    lq = [W.Tq] * W.B if w["lens"] is None else [int(min(max(x, 0), W.Tq)) if W.Tq == W.Tk else W.Tq for x in w["lens"]]
+    rows = sampled_rows(W.B, W.Hq, W.Tq, lq, n_rows, 3)
+    if W.dtype == "e4m3":
+        o_ref, l_ref = oracle.attention_rows_fp8(w["q"], w["k"], w["v"], rows, *w["fp8_scales"], W.scale, W.causal,
+                                                 w["lens"])
+    else:
+        o_ref, l_ref = oracle.attention_rows(w["q"], w["k"], w["v"], rows, W.scale, W.causal, w["lens"])
+    import torch
+
+    idx = tuple(torch.as_tensor(a, device=o.device) for a in np.array(rows).T)
+    return _errors(o[idx], lse[idx], o_ref, l_ref, TOL[W.dtype], f"{len(rows)} sampled rows")
+
+
+def decode_errors(dec, n_seq=3):
+    import oracle
+
+    w, W = dec["w"], dec["W"]
+    o, lse = dec["out"]
+    lens = w["lens"]
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), W.B // 2})[:n_seq]
+    if W.dtype == "e4m3":
+        o_ref = np.zeros((len(pick), W.Hq, W.D))
+        l_ref = np.zeros((len(pick), W.Hq))
+        for n, b in enumerate(pick):
+            ob, lb = oracle.decode_fp8(w["q"][b:b + 1].cpu(), w["k"][b:b + 1].cpu(), w["v"][b:b + 1].cpu(),
+                                       lens[b:b + 1], *w["fp8_scales"], W.scale)
+            o_ref[n], l_ref[n] = ob[0], lb[0]
+    else:
+        ob, lb = oracle.decode(w["q"].cpu(), w["k"], w["v"], lens, W.scale, batches=pick)
+        o_ref, l_ref = ob[pick], lb[pick]
+    return _errors(o[pick], lse[pick], o_ref, l_ref, TOL[W.dtype], f"sequences {pick} (all query heads)")
+
+
+def prefill_entry(torch, name, steps, warmup, calls, args, headline=False):
+    pre = setup_prefill(torch, name)
+    runner = Graphed(torch, pre["step"], calls)
+    check_graph_replay(torch, runner, pre["step"], pre["out"])
+    ev_ms, wall_ms, n = time_steps(torch, runner, steps, warmup, pre["step"])
+    W = pre["W"]
+    kname = "fwd_f32_kernel" if W.dtype == "f32" else "fwd_bf16_kernel"
+    peak = {"bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_MFMA_TFLOPS, "e4m3": PEAK_FP8_BF16_TFLOPS}[W.dtype]
+    flops = pre["flops"]
+    achieved = flops / (ev_ms * 1e-3) / 1e12
+    e = dict(workload=W.note, value=round(flops / (wall_ms * 1e-3) / 1e12, 3), unit="TFLOP/s", steps=n,
+             warmup=warmup, ms_per_step=round(wall_ms, 5), dtype=W.dtype, flops_per_step=flops,
+             roofline=dict(bound="mfma", achieved=round(achieved, 3), peak=round(peak, 1), unit="TFLOP/s",
+                           frac=round(achieved / peak, 4), traffic=traffic_for(kname, name),
+                           mfma_busy=mfma_busy_for(kname, name), kernel=kname, kernel_ms=round(ev_ms, 5)))
+    if W.dtype == "e4m3":
+        e["roofline"]["peak_note"] = "Q K^T on fp8 (5033 TFLOP/s), P V on bf16 (2517)"
+    if W.dtype == "f32":
+        e["roofline"]["peak_note"] = "fp32 matrix peak; 33.6 Mflop per step, launch-latency bound"
+    e["parity"] = prefill_errors(pre, args.check_rows)
+    del runner, pre
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        e["cpu_baseline"] = cpu_baseline_prefill(name, args.cpu_budget)
+    return e
+
+
+def decode_entry(torch, name, steps, warmup, calls, args):
+    paged = name == "decode-paged"
+    dec = (setup_decode_paged(torch, args.page_size) if paged else
+           setup_decode_fp8(torch) if name == "decode-fp8" else setup_decode(torch))
+    runner = Graphed(torch, dec["step"], calls)
+    check_graph_replay(torch, runner, dec["step"], dec["out"])
+    ev_ms, wall_ms, n = time_steps(torch, runner, steps, warmup, dec["step"])
+    W = dec["W"]
+    achieved = dec["bytes"] / (ev_ms * 1e-3) / 1e9
+    note = W.note + (f", paged cache (page size {args.page_size}, pages placed at random)" if paged else "")
+    e = dict(workload=note, value=round(dec["bytes"] / (wall_ms * 1e-3) / 1e9, 2), unit="GB/s", steps=n,
+             warmup=warmup, ms_per_step=round(wall_ms, 5), dtype=W.dtype, bytes_per_step=dec["bytes"],
+             sum_lengths=int(np.sum(dec["w"]["lens"])),
+             roofline=dict(bound="hbm", achieved=round(achieved, 2), peak=PEAK_HBM_GBS, unit="GB/s",
+                           frac=round(achieved / PEAK_HBM_GBS, 4),
+                           traffic=None if paged else traffic_for("decode_split_kernel", name),
+                           kernels="decode_split + decode_merge", kernel_ms=round(ev_ms, 5)))
+    if not paged:
+        e["parity"] = decode_errors(dec)
+    if not args.no_cpu_baseline and not paged:
+        e["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
+    del runner, dec
+    torch.cuda.empty_cache()
+    return e
+
+
+def backward_entry(torch, name, steps, warmup, calls, args):
+    bw = setup_backward(torch, name)
+    runner = Graphed(torch, bw["step"], calls)
+    check_graph_replay(torch, runner, bw["step"], bw["out"])
+    ev_ms, wall_ms, n = time_steps(torch, runner, steps, warmup, bw["step"])
+    W = bw["W"]
+    achieved = bw["flops"] / (ev_ms * 1e-3) / 1e12
+    e = dict(workload=W.note + " (gradients dQ, dK, dV)", value=round(bw["flops"] / (wall_ms * 1e-3) / 1e12, 3),
+             unit="TFLOP/s", steps=n, warmup=warmup, ms_per_step=round(wall_ms, 5), dtype="bf16",
+             flops_per_step=bw["flops"],
+             roofline=dict(bound="mfma", achieved=round(achieved, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                           frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                           traffic=backward_traffic(name), kernels="bwd_prep + bwd_dq + bwd_dkdv",
+                           kernel_ms=round(ev_ms, 5)))
+    e["parity"] = backward_errors(bw, args.check_rows)
+    del runner, bw
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        e["cpu_baseline"] = cpu_baseline_backward(name, args.cpu_budget)
+    return e
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="causal",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long",
                     choices=["causal", "long", "ragged", "decode", "decode-paged", "decode-fp8", "causal-fp8",
                              "long-fp8", "single"])
+    ap.add_argument("--only", action="store_true", help="measure only --workload (no extra keys)")
     ap.add_argument("--page-size", type=int, default=16, help="page size of --workload decode-paged")
-    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurements of the default run")
     ap.add_argument("--backward", action="store_true",
                     help="time the gradients (attn_bwd) of the prefill workload instead of its forward")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement of the default run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time per baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time per baseline")
+    ap.add_argument("--check-rows", type=int, default=256, help="sampled rows for the error report")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB copy (for scaling the FETCH_SIZE/WRITE_SIZE counters)")
     ap.add_argument("--summarize-pmc", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -574,139 +819,44 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     launch_table = f"{ea.attn_tile_table_size()} tuned entries" if ea.attn_tile_table_size() else "built-in rule"
     torch.cuda.set_device(0)
-
-    line = {}
-    if args.workload in ("decode", "decode-paged", "decode-fp8"):
-        paged = args.workload == "decode-paged"
-        fp8 = args.workload == "decode-fp8"
-        dec = (setup_decode_paged(torch, args.page_size) if paged else
-               setup_decode_fp8(torch) if fp8 else setup_decode(torch))
-        runner = Graphed(torch, dec["step"])
-        check_graph_replay(torch, runner, dec["step"], dec["out"])
-        ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
-        gbs = dec["bytes"] / (ms * 1e-3) / 1e9
-        W = dec["W"]
-        note = W.note + (f", paged cache (page size {args.page_size}, pages placed at random)" if paged else "")
-        line = dict(metric="decode KV GB/s (% HBM peak)", value=round(gbs, 2), unit="GB/s", n_gpus=1, steps=n,
-                    warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak",
-                    vs_baseline=None, dtype="e4m3" if fp8 else "bf16", data="synthetic",
-                    config=dict(workload=note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, S_max=W.Tk, D=W.D,
-                                sum_lengths=int(np.sum(dec["w"]["lens"])), parallelism="single GPU",
-                                launch_table=launch_table),
-                    roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                  frac=round(gbs / PEAK_HBM_GBS, 4),
-                                  traffic=None if paged else traffic_for("decode_split_kernel", args.workload),
-                                  kernels="decode_split + decode_merge"))
-        if not args.no_cpu_baseline and not paged:
-            line["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
-        print(json.dumps(line), flush=True)
-        return
-
+    # the headline: exactly K steps of the named workload, in one graph of K calls
+    K, Wm = max(1, args.steps), max(0, args.warmup)
+    name = args.workload
     if args.backward:
-        bw = setup_backward(torch, args.workload)
-        runner = Graphed(torch, bw["step"])
-        check_graph_replay(torch, runner, bw["step"], bw["out"])
-        ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
-        W = bw["W"]
-        tflops = bw["flops"] / (ms * 1e-3) / 1e12
-        line = dict(metric="prefill backward TFLOP/s (% bf16 MFMA peak)", value=round(tflops, 3), unit="TFLOP/s",
-                    n_gpus=1, steps=n, warmup=args.warmup, ms_per_step=round(wall_ms, 5), higher_is_better=True,
-                    scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-                    config=dict(workload=W.note + " (gradients)", B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk,
-                                D=W.D, causal=W.causal, flops_per_step=bw["flops"], parallelism="single GPU"),
-                    roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                                  frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
-                                  kernels="bwd_prep + bwd_dq + bwd_dkdv", kernel_ms=round(ms, 5)))
-        if not args.no_cpu_baseline:
-            line["cpu_baseline"] = cpu_baseline_backward(args.workload, args.cpu_budget)
-        print(json.dumps(line), flush=True)
-        return
+        head = backward_entry(torch, name, K, Wm, K, args)
+        metric = "prefill backward TFLOP/s (% bf16 MFMA peak)"
+    elif name.startswith("decode"):
+        head = decode_entry(torch, name, K, Wm, K, args)
+        metric = "decode KV GB/s (% HBM peak)"
+    else:
+        head = prefill_entry(torch, name, K, Wm, K, args)
+        metric = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+    from exact_tiled_attention_13_amd import workloads as wl
 
-    pre = setup_prefill(torch, args.workload)
-    runner = Graphed(torch, pre["step"])
-    check_graph_replay(torch, runner, pre["step"], pre["out"])
-    ms, wall_ms, n = time_steps(torch, runner, args.steps, args.warmup)
-    W = pre["W"]
-    kname = "fwd_f32_kernel" if W.dtype == "f32" else "fwd_bf16_kernel"
-    tflops = pre["flops"] / (ms * 1e-3) / 1e12
-    peak = {"bf16": PEAK_BF16_TFLOPS, "f32": PEAK_F32_MFMA_TFLOPS, "e4m3": PEAK_FP8_BF16_TFLOPS}[W.dtype]
-    line = dict(
-        metric="prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)",
-        value=round(tflops, 3), unit="TFLOP/s", n_gpus=1, steps=n, warmup=args.warmup,
-        ms_per_step=round(wall_ms, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
-        dtype=W.dtype, data="synthetic",
-        config=dict(workload=W.note, B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk, D=W.D, causal=W.causal,
-                    flops_per_step=pre["flops"], parallelism="single GPU", launch_table=launch_table),
-        roofline=dict(bound="mfma", achieved=round(tflops, 3), peak=peak, unit="TFLOP/s",
-                      frac=round(tflops / peak, 4), traffic=traffic_for(kname, args.workload), kernel=kname,
-                      kernel_ms=round(ms, 5), mfma_busy=mfma_busy_for(kname, args.workload)),
-    )
-    del pre, runner
-    if args.workload == "causal" and not args.no_decode:
-        torch.cuda.empty_cache()
-        dec = setup_decode(torch)
-        drun = Graphed(torch, dec["step"])
-        check_graph_replay(torch, drun, dec["step"], dec["out"])
-        dms, dwall, dn = time_steps(torch, drun, max(20, args.steps // 4), max(5, args.warmup // 4))
-        gbs = dec["bytes"] / (dms * 1e-3) / 1e9
-        DW = dec["W"]
-        line["decode"] = dict(workload=DW.note, value=round(gbs, 2), unit="GB/s", steps=dn, ms_per_step=round(dms, 5),
-                              bytes_per_step=dec["bytes"], sum_lengths=int(np.sum(dec["w"]["lens"])),
-                              roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                            frac=round(gbs / PEAK_HBM_GBS, 4),
-                                            traffic=traffic_for("decode_split_kernel", "decode"),
-                                            kernels="decode_split + decode_merge"))
-        if not args.no_cpu_baseline:
-            line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget / 2)
-        del dec, drun
-        torch.cuda.empty_cache()
-        dec = setup_decode_fp8(torch)
-        drun = Graphed(torch, dec["step"])
-        check_graph_replay(torch, drun, dec["step"], dec["out"])
-        dms, dwall, dn = time_steps(torch, drun, max(20, args.steps // 4), max(5, args.warmup // 4))
-        gbs = dec["bytes"] / (dms * 1e-3) / 1e9
-        DW = dec["W"]
-        line["decode_fp8"] = dict(workload=DW.note, value=round(gbs, 2), unit="GB/s", steps=dn,
-                                  ms_per_step=round(dms, 5), bytes_per_step=dec["bytes"],
-                                  sum_lengths=int(np.sum(dec["w"]["lens"])), dtype="e4m3",
-                                  roofline=dict(bound="hbm", achieved=round(gbs, 2), peak=PEAK_HBM_GBS, unit="GB/s",
-                                                frac=round(gbs / PEAK_HBM_GBS, 4),
-                                                traffic=traffic_for("decode_split_kernel", "decode-fp8"),
-                                                kernels="decode_split + decode_merge"))
-        del dec, drun
-    if args.workload == "causal" and not args.no_decode:
-        # the same causal prefill on E4M3 inputs
-        torch.cuda.empty_cache()
-        pf = setup_prefill(torch, "causal-fp8")
-        prun = Graphed(torch, pf["step"])
-        check_graph_replay(torch, prun, pf["step"], pf["out"])
-        pms, pwall, pn = time_steps(torch, prun, max(20, args.steps // 4), max(5, args.warmup // 4))
-        ptf = pf["flops"] / (pms * 1e-3) / 1e12
-        line["prefill_fp8"] = dict(workload=pf["W"].note, value=round(ptf, 3), unit="TFLOP/s", steps=pn,
-                                   ms_per_step=round(pms, 5), flops_per_step=pf["flops"], dtype="e4m3",
-                                   roofline=dict(bound="mfma", achieved=round(ptf, 3),
-                                                 peak=round(PEAK_FP8_BF16_TFLOPS, 1), unit="TFLOP/s",
-                                                 frac=round(ptf / PEAK_FP8_BF16_TFLOPS, 4),
-                                                 traffic=traffic_for("fwd_bf16_kernel", "causal-fp8"),
-                                                 mfma_busy=mfma_busy_for("fwd_bf16_kernel", "causal-fp8"),
-                                                 kernel="fwd_bf16_kernel (E4M3 instance)",
-                                                 peak_note="Q K^T on fp8 (5033 TFLOP/s), P V on bf16 (2517)"))
-        del pf, prun
-    if args.workload == "causal" and not args.no_backward:
-        torch.cuda.empty_cache()
-        bw = setup_backward(torch, "causal")
-        brun = Graphed(torch, bw["step"])
-        check_graph_replay(torch, brun, bw["step"], bw["out"])
-        bms, bwall, bn = time_steps(torch, brun, max(20, args.steps // 4), max(5, args.warmup // 4))
-        btf = bw["flops"] / (bms * 1e-3) / 1e12
-        line["backward"] = dict(workload=bw["W"].note + " (gradients dQ, dK, dV)", value=round(btf, 3),
-                                unit="TFLOP/s", steps=bn, ms_per_step=round(bms, 5), flops_per_step=bw["flops"],
-                                roofline=dict(bound="mfma", achieved=round(btf, 3), peak=PEAK_BF16_TFLOPS,
-                                              unit="TFLOP/s", frac=round(btf / PEAK_BF16_TFLOPS, 4), traffic=None,
-                                              kernels="bwd_prep + bwd_dq + bwd_dkdv"))
-        del bw, brun
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_prefill(args.workload, args.cpu_budget)
+    W = wl.WORKLOADS[name]
+    line = dict(metric=metric, value=head["value"], unit=head["unit"], n_gpus=1, steps=head["steps"],
+                warmup=head["warmup"], ms_per_step=head["ms_per_step"], higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype=head["dtype"], data="synthetic",
+                config=dict(workload=head["workload"], B=W.B, Hq=W.Hq, Hkv=W.Hkv, Tq=W.Tq, Tk=W.Tk, D=W.D,
+                            causal=W.causal, parallelism="single GPU", launch_table=launch_table,
+                            timing="value = work per step / ms_per_step (wall clock of exactly `steps` graph-replayed "
+                                   "steps between device synchronisations); roofline.achieved = work / "
+                                   "roofline.kernel_ms (HIP events on the kernels' stream, same steps)"),
+                roofline=head["roofline"], parity=head["parity"], context=CONTEXT)
+    for key in ("flops_per_step", "bytes_per_step", "sum_lengths"):
+        if key in head:
+            line["config"][key] = head[key]
+    if "cpu_baseline" in head:
+        line["cpu_baseline"] = head["cpu_baseline"]
+    if not args.only and not args.backward and name == "long":
+        ex = max(20, K)
+        line["causal"] = prefill_entry(torch, "causal", 10 * ex, 5, 20, args)
+        line["ragged"] = prefill_entry(torch, "ragged", 2 * ex, 5, 20, args)
+        line["decode"] = decode_entry(torch, "decode", ex, 5, 20, args)
+        line["decode_fp8"] = decode_entry(torch, "decode-fp8", ex, 5, 20, args)
+        line["prefill_fp8"] = prefill_entry(torch, "long-fp8", ex, 3, 20, args)
+        line["backward"] = backward_entry(torch, "causal", 2 * ex, 5, 20, args)
+        line["single"] = prefill_entry(torch, "single", 10 * ex, 5, 20, args)
     print(json.dumps(line), flush=True)
 
 

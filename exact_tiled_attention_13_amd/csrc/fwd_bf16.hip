@@ -132,7 +132,6 @@ __device__ __forceinline__ void wait_tile(int rem) {
   }
 }
 
-typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
 typedef __attribute__((address_space(3))) const u16 lds_u16;
 typedef __attribute__((address_space(3))) const uint8_t lds_u8;
@@ -238,12 +237,14 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // 16 ks + 8 h .. +7.  E4M3: bytes 64 kk + 32 h .. +31; the K fragments
   // use the same bytes of their rows, so every column is paired once.
   // Lanes past Tq read row Tq-1 (their results are never stored), so the
-  // loads are unconditional and issue back to back.  A negative score
-  // factor flips the sign bits of Q, after the first K/V copies are issued
-  // (flip_q below), so that waiting for Q does not hold up those copies.
+  // loads are unconditional and issue back to back.  They are issued after
+  // the first K/V copies (load_q below) and waited for once, in a wait the
+  // compiler sees, so that no wait for Q (which would also wait for every
+  // copy in flight) is placed inside the loop.  A negative score factor
+  // flips the sign bits of Q (flip_q).
   bf16x8 qf[FP8 ? 1 : C::KS];
   i32x8 qf8[FP8 ? C::KK : 1];
-  {
+  auto load_q = [&]() {
     const int qsrc = min(qrow, Tq - 1);
     if constexpr (FP8) {
       const u32x4* src = reinterpret_cast<const u32x4*>(Qp + (size_t)qsrc * D + 32 * h);
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, src[2 * ks]);
     }
-  }
+  };
   auto flip_q = [&]() {
     if constexpr (FP8) {
 #pragma unroll
@@ -290,6 +291,15 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // that offset against the last chunk of row Lk-1 (rows at or past Lk
   // read finite data, and those keys are masked) plus the load, addressed
   // as scalar base + 32-bit lane offset.
+  //
+  // The copy is written as inline asm (M0 = the LDS destination, then
+  // global_load_lds_dwordx4) rather than with the compiler builtin: with an
+  // LDS write in flight that it can see, the compiler's wait insertion
+  // waits for every outstanding LDS read (lgkmcnt(0)) before each use of a
+  // fragment, where a count (lgkmcnt(N)) suffices; measured 2-6% faster.
+  // The copies are ordered against the reads by the loop's explicit vmcnt
+  // waits and barriers, as before.  No other instruction of these kernels
+  // uses M0 (checked in the generated code), so clobbering it is safe.
   constexpr int RB = D * C::ESZ;   // bytes per row
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
   uint32_t dma_off[C::VMEM_PER_TILE];
@@ -314,8 +324,14 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     for (int i = 0; i < C::VMEM_PER_TILE; ++i) {
       const int ci = (wg + NWG * i) % (2 * C::LOADS);
       const int t = ci / C::LOADS, li = ci - t * C::LOADS;
-      const uint8_t* g = (t ? Vp : Kp) + (size_t)kb * RB + min(dma_off[i], lim);
-      __builtin_amdgcn_global_load_lds((gptr_t*)g, (lptr_t*)(ring8 + (st * 2 + t) * C::TB + li * 1024), 16, 0, 0);
+      const uint8_t* gb = (t ? Vp : Kp) + (size_t)kb * RB;
+      const uint32_t la = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(size_t)(lptr_t*)(ring8 + (st * 2 + t) * C::TB + li * 1024));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // M0 on the clobber list: see above
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(la), "v"(min(dma_off[i], lim)), "s"(gb) : "memory", "m0");
+#pragma clang diagnostic pop
     }
   };
 
@@ -444,6 +460,69 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
     lsum = ls;
   };
 
+  // ---- pieces of the pipelined bf16 loop.  exp_tile: P = exp2(c s - m)
+  // of a tile, written back over its scores (kept for the row sum) and
+  // packed to bf16 MFMA operands in pf; sum_tile: the row sums of those P,
+  // added in the order do_exp adds them; raw_max: the per-lane maximum of
+  // raw scores; mask_tile: the boundary-tile mask of do_max; finish_max: the
+  // row maximum across the wave halves and the lazy rescale of do_max.
+  auto exp_tile = [&](f32x16* sd) {
+    const float nm = (m == kNegInf) ? 0.f : -m;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(sd[kb][8 * sh + e], c, nm));
+          const float p1 = fast_exp2(__builtin_fmaf(sd[kb][8 * sh + e + 1], c, nm));
+          sd[kb][8 * sh + e] = p0;
+          sd[kb][8 * sh + e + 1] = p1;
+          pk[e >> 1] = pack2_bf16(p0, p1);
+        }
+        pf[kb][sh] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      }
+  };
+  auto sum_tile = [&](const f32x16* sd) {
+    float ls = lsum;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ls += sd[kb][r];
+    lsum = ls;
+  };
+  auto raw_max = [&](const f32x16* sd) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, sd[kb][r]), sd[kb][r + 1]);
+    return mx;
+  };
+  auto mask_tile = [&](f32x16* sd, int kbase) {
+    const int lim = CAUSAL ? min(Lk - 1, qrow + off) : Lk - 1;
+    const int rel = lim - kbase - 4 * h;
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        sd[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3)) <= rel ? sd[kb][r] : kNegInf;
+  };
+  auto finish_max = [&](float mx) {
+    mx = xhalf_max(mx);
+    const float mt = (mx == kNegInf) ? kNegInf : mx * c;
+    const bool grow = mt > m + kThresh;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - ((mnew == kNegInf) ? 0.f : mnew));
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] *= alpha;
+    }
+  };
+
   // ---- E4M3: widen the V tile of stage stv into bf16 buffer vw (the layout
   // of a bf16 V stage).  Each thread of the key group takes WE consecutive
   // elements of one row.
@@ -492,6 +571,8 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   if (ntiles_all > 0) {
 #pragma unroll
   for (int p = 0; p < C::NS - 1; ++p) issue(p, p);
+  load_q();
+  wait_vm_lds<0>();
   if (negq) flip_q();
   if constexpr (C::PIPE) {
     // Iteration lt computes P of tile lt, the scores of tile lt+1 and
@@ -524,13 +605,30 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
       if constexpr (FP8)
         if (lt + 1 < ntiles) widen((lt + 1) % C::NS, (lt + 1) & 1);
       if (lt >= ntiles || kb_of(lt) > kmax) return;   // wave-uniform
-      do_exp(sc);
-      do_scores((lt + 1) % C::NS, sn);
-      if constexpr (FP8)
+      if constexpr (FP8) {
+        do_exp(sc);
+        do_scores((lt + 1) % C::NS, sn);
         do_pv(vwide + (lt & 1) * C::TILE);
-      else
+        if (lt + 1 < ntiles && kb_of(lt + 1) <= kmax) do_max(sn, kb_of(lt + 1));
+      } else {
+        // bf16: P of tile lt with the scores of tile lt+1, then O += V P of
+        // tile lt, then the row sums of tile lt and the raw row maximum of
+        // tile lt+1 (their VALU work overlaps the P V products); the mask
+        // (boundary tiles only) and the lazy rescale follow
+        exp_tile(sc);
+        do_scores((lt + 1) % C::NS, sn);
         do_pv(ring + ((lt % C::NS) * 2 + 1) * C::TILE);
-      if (lt + 1 < ntiles && kb_of(lt + 1) <= kmax) do_max(sn, kb_of(lt + 1));
+        sum_tile(sc);
+        float mx = raw_max(sn);
+        if (lt + 1 < ntiles && kb_of(lt + 1) <= kmax) {
+          const int kb1 = kb_of(lt + 1);
+          if (kb1 + C::BN - 1 > kfull) {
+            mask_tile(sn, kb1);
+            mx = raw_max(sn);
+          }
+          finish_max(mx);
+        }
+      }
     };
     for (int lt = 0; lt < per; lt += 2) {
       step(lt, s[0], s[1]);

@@ -26,7 +26,7 @@ def _gpu():
 
 
 def force(op, dtype, D, causal, v0, v1):
-    _lib.attn_set_tile_table([[op, dtype, D, causal, 0, 2**31 - 1, v0, v1]])
+    _lib.attn_set_tile_table([[op, dtype, D, causal, 0, 2**31 - 1, 0, 2**31 - 1, v0, v1]])
 
 
 def check(o, lse, o_ref, l_ref, what):
