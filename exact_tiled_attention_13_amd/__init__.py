@@ -32,6 +32,8 @@ from ._lib import (  # noqa: F401
     attn_bwd_workspace_size,
     attn_decode,
     attn_decode_fp8,
+    attn_decode_noalloc,
+    attn_decode_noalloc_max_bytes,
     attn_decode_paged,
     attn_decode_paged_fp8,
     attn_decode_workspace_size,
@@ -44,7 +46,8 @@ from ._lib import (  # noqa: F401
     load,
 )
 
-__all__ = ["fwd", "fwd_fp8", "decode", "decode_paged", "decode_fp8", "decode_paged_fp8", "bwd", "attn_fwd", "attn_decode",
+__all__ = ["fwd", "fwd_fp8", "decode", "decode_noalloc", "attn_decode_noalloc", "attn_decode_noalloc_max_bytes",
+           "decode_paged", "decode_fp8", "decode_paged_fp8", "bwd", "attn_fwd", "attn_decode",
            "attn_decode_paged", "attn_decode_fp8", "attn_decode_paged_fp8", "attn_fwd_fp8",
            "attn_decode_workspace_size", "attn_bwd",
            "attn_bwd_workspace_size", "attn_set_tile_table", "attn_tile_table_size", "attn_tile_choice",
@@ -212,6 +215,35 @@ def decode(q, k_cache, v_cache, kv_lens, *, scale: float | None = None, workspac
     attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(), l_out.data_ptr(), B, Hq, Hkv,
                 S_max, D, scale, lens.data_ptr(), ws_ptr, ws_bytes, dt, stream)
     return o, l_out
+
+
+def decode_noalloc(q, k_cache, v_cache, kv_lens, *, out, lse, scale: float | None = None):
+    """decode() through attn_decode_noalloc: the library's fixed scratch
+    replaces the workspace, and the caller passes the outputs, so the call
+    allocates no device memory (usable under graph capture).  kv_lens must be
+    an int32 tensor on q's device.  Returns (out, lse)."""
+    torch = _torch()
+    dt = _dtype_code(q)
+    _on_gpu(q)
+    _check_tensor("q", q, 3, q.dtype, q.device)
+    B, Hq, D = q.shape
+    _check_tensor("k_cache", k_cache, 4, q.dtype, q.device)
+    _check_tensor("v_cache", v_cache, 4, q.dtype, q.device)
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != D:
+        raise ValueError("cache shapes do not match q")
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if not isinstance(kv_lens, torch.Tensor):
+        raise ValueError("kv_lens must be an int32 tensor on the GPU of q (no copy is made here)")
+    lens = _lens(kv_lens, B, q.device, True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check_tensor("out", out, 3, q.dtype, q.device, shape=(B, Hq, D))
+    _check_tensor("lse", lse, 2, torch.float32, q.device, shape=(B, Hq), align=4)
+    _no_alias([("out", out), ("lse", lse)], [("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("kv_lens", lens)])
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                        Hkv, S_max, D, scale, lens.data_ptr(), dt, stream)
+    return out, lse
 
 
 def _block_table(block_table, B, device):

@@ -19,7 +19,8 @@ MIATTN_TILE_FIELDS = 10
 
 EXPORTED = ("attn_fwd", "attn_fwd_fp8", "attn_decode_workspace_size", "attn_decode", "attn_decode_paged", "attn_decode_fp8",
             "attn_decode_paged_fp8", "attn_bwd_workspace_size", "attn_bwd", "attn_set_tile_table",
-            "attn_tile_table_size", "attn_tile_choice", "attn_strerror", "attn_abi_version")
+            "attn_tile_table_size", "attn_tile_choice", "attn_strerror", "attn_abi_version",
+            "attn_decode_noalloc", "attn_decode_noalloc_max_bytes")
 
 _lib = None
 
@@ -51,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.attn_decode_workspace_size.restype = sz
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, sz, i, vp]
     lib.attn_decode.restype = i
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
+    lib.attn_decode_noalloc.restype = i
+    lib.attn_decode_noalloc_max_bytes.argtypes = []
+    lib.attn_decode_noalloc_max_bytes.restype = sz
     lib.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp, sz, i, vp]
     lib.attn_decode_paged.restype = i
     lib.attn_decode_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp, vp, sz, vp]
@@ -123,6 +128,18 @@ def attn_decode(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, D, scale, kv_len
                               S_max, D, float(scale), kv_lens or None, workspace or None, workspace_bytes, dtype,
                               stream or None)
     return _check(code) if check else code
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, D, scale, kv_lens, dtype, stream,
+                        check=True):
+    """Raw C-ABI call; pointers are integers (0 = NULL)."""
+    code = load().attn_decode_noalloc(q or None, k_cache or None, v_cache or None, o or None, lse or None, B, Hq,
+                                      Hkv, S_max, D, float(scale), kv_lens or None, dtype, stream or None)
+    return _check(code) if check else code
+
+
+def attn_decode_noalloc_max_bytes() -> int:
+    return int(load().attn_decode_noalloc_max_bytes())
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Tq, Tk, D, scale, causal, kv_lens, workspace,

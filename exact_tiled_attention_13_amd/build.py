@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmiattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "tiles.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip"]
+SOURCES = ["api.cpp", "tiles.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "noalloc.hip"]
 
 # Per-file flags.  The bf16 prefill kernel never lets NaN reach its softmax
 # (rows past a sequence's length are replaced by finite rows before the

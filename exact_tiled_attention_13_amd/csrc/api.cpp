@@ -35,6 +35,8 @@ bool fp8_scales_ok(float scale, float q_scale, float k_scale, float v_scale) {
 
 namespace miattn {
 
+int record_hip_error(hipError_t e) { return hip_fail(e); }
+
 int device_cu_count() {
   // Per-device cache.  Threads that race on a device's first call all store
   // the same value; relaxed atomics make that race well defined.
@@ -65,6 +67,8 @@ const char* attn_strerror(int code) {
     case MIATTN_ERR_HIP: return g_hip_msg;
     case MIATTN_ERR_ALIGN:
       return "misaligned pointer (tensors and workspaces need 16-byte alignment; lse, kv_lens and block_table 4)";
+    case MIATTN_ERR_SCRATCH:
+      return "the call needs more scratch than attn_decode_noalloc holds (attn_decode_noalloc_max_bytes)";
     default: return "unknown error code";
   }
 }
@@ -107,6 +111,15 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int S_max, int D) {
 
 namespace {
 
+// Grid limits of the split-K decode.
+int decode_limits(int B, int Hq, int Hkv, int S_max) {
+  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
+  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
+  // work items (sequence, head block, split) are counted in int32
+  if ((long long)B * gy * miattn::decode_num_splits(S_max) > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
+  return MIATTN_OK;
+}
+
 // Checks and launches shared by the four decode entry points.  Contiguous
 // caches pass block_table = NULL; E4M3 caches pass fp8 = 1 and their scales.
 int decode_common(const void* q, const void* k, const void* v, const int32_t* block_table, void* o, float* lse,
@@ -116,10 +129,8 @@ int decode_common(const void* q, const void* k, const void* v, const int32_t* bl
   const size_t need = attn_decode_workspace_size(B, Hq, Hkv, S_max, D);
   if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;
   if (!a16(workspace)) return MIATTN_ERR_ALIGN;
-  const long long gy = (long long)Hkv * ((Hq / Hkv + 15) / 16);
-  if (gy > 65535 || B > 65535) return MIATTN_ERR_SHAPE;
-  // work items (sequence, head block, split) are counted in int32
-  if ((long long)B * gy * miattn::decode_num_splits(S_max) > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
+  const int lim = decode_limits(B, Hq, Hkv, S_max);
+  if (lim != MIATTN_OK) return lim;
   float* ws = static_cast<float*>(workspace);
   const size_t nsp = (size_t)B * Hq * miattn::decode_num_splits(S_max);
   int32_t* idx = reinterpret_cast<int32_t*>(ws + nsp * (D + 2));
@@ -145,17 +156,33 @@ int paged_geometry(int num_pages, int page_size, int max_blocks, int Hkv, int* s
 
 }  // namespace
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
-                int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, void* workspace,
-                size_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace miattn {
+
+// Every check of attn_decode except the workspace's (no HIP call).
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const void* o, const float* lse, int B,
+                 int Hq, int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, int dtype) {
   if (!q || !k_cache || !v_cache || !o || !kv_lens) return MIATTN_ERR_NULL;
   if (!a16(q) || !a16(k_cache) || !a16(v_cache) || !a16(o) || !a4(lse) || !a4(kv_lens)) return MIATTN_ERR_ALIGN;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S_max <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
   if (!supported_d(D) || (dtype != MIATTN_F32 && dtype != MIATTN_BF16)) return MIATTN_ERR_UNSUPPORTED;
+  if (dtype == MIATTN_F32) return (long long)B * Hq > 0x7fffffffLL ? MIATTN_ERR_SHAPE : MIATTN_OK;
+  return decode_limits(B, Hq, Hkv, S_max);
+}
+
+}  // namespace miattn
+
+extern "C" {
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int Hq,
+                int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, void* workspace,
+                size_t workspace_bytes, int dtype, void* stream) {
+  const int chk = miattn::decode_check(q, k_cache, v_cache, o, lse, B, Hq, Hkv, S_max, D, scale, kv_lens, dtype);
+  if (chk != MIATTN_OK) return chk;
   if (dtype == MIATTN_F32) {
     // one query row against the cache, bottom-right causal: exactly the decode step
-    if ((long long)B * Hq > 0x7fffffffLL) return MIATTN_ERR_SHAPE;
     miattn::FwdArgs a{q, k_cache, v_cache, o, lse, kv_lens, B, Hq, Hkv, 1, S_max, D, scale, 1};
     hipError_t e = miattn::launch_fwd_f32(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? MIATTN_OK : hip_fail(e);

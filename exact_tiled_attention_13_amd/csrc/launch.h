@@ -83,6 +83,13 @@ inline size_t decode_ws_floats(int B, int Hq, int S_max, int D) {
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cu_count();
 
+// Records a HIP error for attn_strerror and returns MIATTN_ERR_HIP (api.cpp).
+int record_hip_error(hipError_t e);
+
+// Every check of attn_decode except the workspace's; no HIP call (api.cpp).
+int decode_check(const void* q, const void* k_cache, const void* v_cache, const void* o, const float* lse, int B,
+                 int Hq, int Hkv, int S_max, int D, float scale, const int32_t* kv_lens, int dtype);
+
 // Launch choices (tiles.cpp).  Prefill: shape 0 = 256-row workgroups with
 // one key group, 1 = 128-row workgroups with two key groups; zig 0/1, or -1
 // for the built-in rule.  T = Tk (keys per sequence),

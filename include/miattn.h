@@ -79,7 +79,8 @@ enum {
   MIATTN_ERR_UNSUPPORTED = -3, /* D not 64/128, unknown dtype, causal not 0/1 */
   MIATTN_ERR_WORKSPACE = -4,   /* workspace missing or too small */
   MIATTN_ERR_HIP = -5,         /* the HIP runtime refused a launch; see attn_strerror */
-  MIATTN_ERR_ALIGN = -6        /* a pointer is not aligned as required (see Alignment above) */
+  MIATTN_ERR_ALIGN = -6,       /* a pointer is not aligned as required (see Alignment above) */
+  MIATTN_ERR_SCRATCH = -7      /* attn_decode_noalloc: the call needs more than its fixed scratch */
 };
 
 /*
@@ -132,6 +133,26 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o
                 int B, int Hq, int Hkv, int S_max, int D, float scale,
                 const int32_t* kv_lens, void* workspace, size_t workspace_bytes,
                 int dtype, void* stream);
+
+/*
+ * attn_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same operation, arguments (less the
+ * workspace), checks and results as attn_decode; the call allocates nothing.
+ * The split partials go to a fixed scratch array of
+ * attn_decode_noalloc_max_bytes() bytes (96 MiB) that the library holds on
+ * each device it runs on until the process ends; a call whose
+ * attn_decode_workspace_size(B, Hq, Hkv, S_max, D) exceeds it returns
+ * MIATTN_ERR_SCRATCH before any HIP call.  Every call on a device shares that
+ * device's array: calls that overlap on one device (e.g. on two streams
+ * without ordering between them) race and give wrong results; calls ordered
+ * on one stream are fine.  Nothing in the array needs clearing between
+ * calls.
+ */
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                        int B, int Hq, int Hkv, int S_max, int D, float scale,
+                        const int32_t* kv_lens, int dtype, void* stream);
+size_t attn_decode_noalloc_max_bytes(void);
 
 /*
  * One decode step against a paged KV cache: the per-sequence caches live in

@@ -45,7 +45,7 @@ def test_abi_version(lib):
 
 
 def test_strerror_covers_codes(lib):
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert ea.attn_strerror(code)
     assert "unknown" in ea.attn_strerror(-99)
 
@@ -111,6 +111,27 @@ def test_decode_validation(lib, args, code):
              kv_lens=FAKE, workspace=FAKE, workspace_bytes=1 << 40, dtype=1, stream=0)
     a.update(args)
     assert ea.attn_decode(**a, check=False) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(kv_lens=0), -1), (dict(q=0), -1), (dict(v_cache=0), -1), (dict(o=0), -1),
+    (dict(q=ODD4), -6), (dict(lse=ODD), -6), (dict(kv_lens=ODD), -6),
+    (dict(S_max=0), -2), (dict(Hq=5, Hkv=2), -2), (dict(scale=float("nan")), -2),
+    (dict(D=32), -3), (dict(dtype=7), -3),
+    # partials past the fixed scratch: 64 x 64 x 8192 splits x 130 floats
+    (dict(B=64, Hq=64, Hkv=8, S_max=1 << 22), -7),
+])
+def test_decode_noalloc_validation(lib, args, code):
+    a = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, S_max=100, D=128, scale=0.1,
+             kv_lens=FAKE, dtype=1, stream=0)
+    a.update(args)
+    assert ea.attn_decode_noalloc(**a, check=False) == code
+
+
+def test_decode_noalloc_scratch_size(lib):
+    # 96 MiB: the GQA decode workload's partials (64 x 32 x 64 splits x 130 floats) fit
+    assert ea.attn_decode_noalloc_max_bytes() == 96 << 20
+    assert ea.attn_decode_workspace_size(64, 32, 8, 32768, 128) <= ea.attn_decode_noalloc_max_bytes()
 
 
 def test_workspace_size(lib):
