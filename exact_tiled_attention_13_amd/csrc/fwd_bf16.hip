@@ -298,8 +298,11 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   // waits for every outstanding LDS read (lgkmcnt(0)) before each use of a
   // fragment, where a count (lgkmcnt(N)) suffices; measured 2-6% faster.
   // The copies are ordered against the reads by the loop's explicit vmcnt
-  // waits and barriers, as before.  No other instruction of these kernels
-  // uses M0 (checked in the generated code), so clobbering it is safe.
+  // waits and barriers, as before.  An SALU write of M0 needs one wait state
+  // before an LDS DMA reads it (the hardware does not interlock it, and the
+  // compiler's hazard pass does not look inside inline asm), hence the
+  // s_nop.  No other instruction of these kernels uses M0 (checked in the
+  // generated code), so clobbering it is safe.
   constexpr int RB = D * C::ESZ;   // bytes per row
   constexpr int CPR = RB / 16;     // 16-byte chunks per row
   uint32_t dma_off[C::VMEM_PER_TILE];
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
           (uint32_t)(size_t)(lptr_t*)(ring8 + (st * 2 + t) * C::TB + li * 1024));
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // M0 on the clobber list: see above
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                    :: "s"(la), "v"(min(dma_off[i], lim)), "s"(gb) : "memory", "m0");
 #pragma clang diagnostic pop
     }
