@@ -146,55 +146,116 @@ __device__ __forceinline__ P* lds_base(P* p) {
   return p;
 }
 
-template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
-__global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
-    const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
-    u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
-    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int zig, int uorder, float oscale) {
-  using C = FwdCfg<D, NWG, KSPLIT, FP8>;
-  const uint8_t* __restrict__ Q = static_cast<const uint8_t*>(Qv);
-  const uint8_t* __restrict__ K = static_cast<const uint8_t*>(Kv);
-  const uint8_t* __restrict__ V = static_cast<const uint8_t*>(Vv);
-  __shared__ __attribute__((aligned(1024))) u16 smem[C::SMEM];   // [key group][stage][K, V][tile]
+// Orders of the tiles over the workgroup ids (one tile per workgroup; the
+// hardware dispatches ids in increasing order as CUs free up).
+enum : int { ORDER_ID_NATURAL = 0, ORDER_ID_UNITS = 1, ORDER_ID_ZIG = 2, ORDER_ID_LIST = 3 };
+// ragged grids are ordered by work for up to this many sequences (one per lane)
+constexpr int kOrderMaxB = 64;
 
+// Tiles of a sequence with work (key tiles) greater than w, given its valid
+// keys Lk, query tiles with a valid row nq and causal offset off = Lk - Lq.
+// Work is nondecreasing in the tile index, so these are the last ones.
+template <int BM, int BN, bool CAUSAL>
+__device__ __forceinline__ int tiles_above(int Lk, int nq, int off, int w) {
+  if (nq == 0 || (long long)Lk <= (long long)w * BN) return 0;
+  if (!CAUSAL) return nq;
+  // the tile's last row plus off must pass w*BN: (qt+1) BM + off > w BN
+  const long long x = (long long)w * BN - off;
+  const long long qmin = x < 0 ? 0 : x / BM;
+  return (int)max(0LL, (long long)nq - qmin);
+}
+
+// sum over lanes 0..n-1 of a per-lane value, on the scalar unit
+__device__ __forceinline__ int lanes_sum(int v, int n) {
+  int s = 0;
+  for (int l = 0; l < n; ++l) s += __builtin_amdgcn_readlane(v, l);
+  return s;
+}
+
+// Tile list of a ragged grid (lengths in kv_lens, B <= kOrderMaxB):
+// position p -> (b, hq, hk, qt), computed alike by every wave.  Tiles by
+// work (key tiles), most first; ties by sequence, then tile from the last,
+// then query head with the KV head fastest; then the tiles with no work at
+// all (padding rows, rows that see no key), which only write zeros.  Lane l
+// holds sequence l; the sums over sequences run on the scalar unit.
+// Workgroups dispatched in this order fill the chip longest-first, and the
+// short zero-writing ones fill in the tail.
+template <int BM, int BN, bool CAUSAL>
+__device__ __forceinline__ void tile_at(int p, const int32_t* __restrict__ kv_lens, int B, int Hq, int Hkv, int Tq,
+                                        int Tk, int nqt, int& b, int& hq, int& hk, int& qt) {
+  const int G = Hq / Hkv;
+  const int lane = threadIdx.x & 63;
+  int Lk = 0, nq = 0, off = 0;
+  if (lane < B) {
+    Lk = clampi(kv_lens[lane], 0, Tk);
+    const int Lq = (Tq == Tk) ? Lk : Tq;
+    nq = (Lq + BM - 1) / BM;
+    off = Lk - Lq;
+  }
+  const int wmax = (Tk + BN - 1) / BN;
+  const int above0 = tiles_above<BM, BN, CAUSAL>(Lk, nq, off, 0);
+  const int F0 = Hq * lanes_sum(above0, B);
+  int cnt_hi, cnt_lo;   // this lane's tiles with work > w* and > w* - 1
+  int r;                // rank inside the group of work w*
+  const bool zero = p >= F0;
+  if (zero) {
+    r = p - F0;
+    cnt_hi = above0;
+    cnt_lo = 0;
+  } else {
+    // smallest w >= 1 with (tiles of work > w) <= p: the work of p
+    int lo = 1, hi = wmax;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (Hq * lanes_sum(tiles_above<BM, BN, CAUSAL>(Lk, nq, off, mid), B) <= p) hi = mid;
+      else lo = mid + 1;
+    }
+    cnt_hi = tiles_above<BM, BN, CAUSAL>(Lk, nq, off, lo);
+    cnt_lo = tiles_above<BM, BN, CAUSAL>(Lk, nq, off, lo - 1);
+    r = p - Hq * lanes_sum(cnt_hi, B);
+  }
+  // tiles of the group per sequence; the sequence whose range holds r
+  const int mine = zero ? (lane < B ? nqt - cnt_hi : 0) : (cnt_lo - cnt_hi);
+  int l = 0, pre = 0;
+  for (; l < B; ++l) {
+    const int ml = __builtin_amdgcn_readlane(mine, l);
+    if (r < Hq * (pre + ml)) break;
+    pre += ml;
+  }
+  if (l == B) {   // not reached (every position lies in one sequence's range); computes nothing
+    b = 0;
+    hq = 0;
+    hk = 0;
+    qt = nqt;
+    return;
+  }
+  b = l;
+  const int jj = r - Hq * pre;
+  const int t = jj / Hq, hr = jj - t * Hq;
+  const int g = hr / Hkv;
+  hk = hr - g * Hkv;
+  hq = hk * G + g;
+  const int nq_l = __builtin_amdgcn_readlane(nq, l), hi_l = __builtin_amdgcn_readlane(cnt_hi, l);
+  if (zero) {
+    const int zlo = nq_l - hi_l;   // tiles [0, zlo) and [nq, nqt) have no work
+    qt = t < zlo ? t : nq_l + (t - zlo);
+  } else {
+    qt = nq_l - hi_l - 1 - t;      // the group's tiles, last first
+  }
+}
+
+template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
+__device__ __forceinline__ void fwd_tile(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
+    int B, int Hq, int Hkv, int Tq, int Tk, float c, int negq, float oscale, u16* smem, int b, int hq, int hk,
+    int qt) {
+  using C = FwdCfg<D, NWG, KSPLIT, FP8>;
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kg = w / NWG;          // key group
   const int wg = w - kg * NWG;     // wave within the group = its 32-row block
-
-  // Workgroup -> (query tile, batch, head).  Query tiles run from the last
-  // tile down, so under a causal mask the longest tiles start first.  For
-  // grids of several rounds whose (batch, KV head) unit count is a multiple
-  // of 8 (uorder), each XCD gets whole units (below); otherwise the
-  // query-tile index is the slow one and ids sharing a (batch, head) are
-  // B*Hq apart.  When the whole grid is
-  // resident at once (zig), workgroups id and id + grid/2 share a CU, so the
-  // second half of the ids runs from the first tile up: each CU then holds a
-  // long and a short causal tile, equal work in all.
-  const int BH = B * Hq;
-  const int id = blockIdx.x;
-  const int G = Hq / Hkv;
-  int tq_slot, b, hq;
-  if (uorder) {
-    // ids i, i+8, i+16, ... run on one XCD: give each XCD whole (batch, KV
-    // head) units, one unit's query heads and tiles after another, so that
-    // the workgroups resident on an XCD at once share one head's K/V in L2
-    const int xcd = id & 7, k = id >> 3;
-    const int ul = k / (G * nqt), r = k - ul * (G * nqt);
-    tq_slot = r / G;
-    const int u = xcd + 8 * ul;
-    b = u / Hkv;
-    hq = (u - b * Hkv) * G + (r - tq_slot * G);
-  } else {
-    tq_slot = id / BH;
-    const int bh = id - tq_slot * BH;
-    b = bh / Hq;
-    hq = bh - b * Hq;
-  }
-  const int half = (nqt + 1) / 2;
-  const int qt = (zig && tq_slot >= half) ? tq_slot - half : nqt - 1 - tq_slot;
-  const int hk = hq / G;
 
   int Lk = Tk, Lq = Tq;
   if (kv_lens != nullptr) {
@@ -221,6 +282,17 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   if (rows_end > q0) kend = CAUSAL ? min(Lk, rows_end + off) : Lk;
   if (kend < 0) kend = 0;
   const int ntiles_all = (kend + C::BN - 1) / C::BN;
+  if (ntiles_all == 0) {
+    // no row of the tile sees a key (padding rows, or rows before the first
+    // key under the causal alignment): O = 0 and LSE = -inf for its rows,
+    // written as one contiguous block, without touching Q, K, V or LDS
+    const int rows = max(0, min(C::BM, Tq - q0));
+    u32x4* o4 = reinterpret_cast<u32x4*>(Op + (size_t)q0 * D);
+    for (int i = tid; i < rows * D / 8; i += C::NT) o4[i] = u32x4{0u, 0u, 0u, 0u};
+    if (LSE != nullptr)
+      for (int i = tid; i < rows; i += C::NT) LSE[((size_t)b * Hq + hq) * Tq + q0 + i] = kNegInf;
+    return;
+  }
   const int per = (ntiles_all + KSPLIT - 1) / KSPLIT;
   const int ntiles = ntiles_all > kg ? (ntiles_all - kg + KSPLIT - 1) / KSPLIT : 0;
   auto tile_of = [&](int lt) { return lt * KSPLIT + kg; };
@@ -762,6 +834,61 @@ __global__ __launch_bounds__(64 * NWG * KSPLIT) void fwd_bf16_kernel(
   }
 }
 
+// Workgroup id -> (query tile, batch, head).  ORDER_ID_LIST (ragged grids):
+// the id is the position in tile_at's list, longest work first.  Otherwise
+// query tiles run from the last tile down, so under a causal mask the
+// longest tiles start first.  ORDER_ID_UNITS (grids of several rounds whose (batch, KV head)
+// unit count is a multiple of 8): each XCD gets whole units (ids i, i+8,
+// i+16, ... run on one XCD), one unit's query heads and tiles after
+// another, so that the workgroups resident on an XCD at once share one
+// head's K/V in L2.  Otherwise the query-tile index is the slow one and ids
+// sharing a (batch, head) are B*Hq apart.  ORDER_ID_ZIG (the whole grid
+// resident at once): workgroups id and id + grid/2 share a CU, so the
+// second half of the ids runs from the first tile up: each CU then holds a
+// long and a short causal tile, equal work in all.
+// The E4M3 D=128 two-key-group shape fits two workgroups per CU in LDS; it
+// is held to 128 registers per lane (four waves per SIMD) so that two are
+// resident (the D=64 shapes stay below that by themselves).
+template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
+__global__ __launch_bounds__(64 * NWG * KSPLIT)
+__attribute__((amdgpu_waves_per_eu((D == 128 && FP8 && KSPLIT > 1) ? 4 : 1))) void fwd_bf16_kernel(
+    const void* __restrict__ Qv, const void* __restrict__ Kv, const void* __restrict__ Vv,
+    u16* __restrict__ O, float* __restrict__ LSE, const int32_t* __restrict__ kv_lens,
+    int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, int negq, int order, float oscale) {
+  using C = FwdCfg<D, NWG, KSPLIT, FP8>;
+  __shared__ __attribute__((aligned(1024))) u16 smem[C::SMEM];   // [key group][stage][K, V][tile]
+  const int id = blockIdx.x;
+  const int G = Hq / Hkv;
+  if (order == ORDER_ID_LIST) {
+    int b, hq, hk, qt;
+    tile_at<C::BM, C::BN, CAUSAL>(id, kv_lens, B, Hq, Hkv, Tq, Tk, nqt, b, hq, hk, qt);
+    fwd_tile<D, NWG, KSPLIT, CAUSAL, FP8>(static_cast<const uint8_t*>(Qv), static_cast<const uint8_t*>(Kv),
+                                          static_cast<const uint8_t*>(Vv), O, LSE, kv_lens, B, Hq, Hkv, Tq, Tk, c,
+                                          negq, oscale, smem, b, hq, hk, qt);
+    return;
+  }
+  int tq_slot, b, hq;
+  if (order == ORDER_ID_UNITS) {
+    const int xcd = id & 7, k = id >> 3;
+    const int ul = k / (G * nqt), r = k - ul * (G * nqt);
+    tq_slot = r / G;
+    const int u = xcd + 8 * ul;
+    b = u / Hkv;
+    hq = (u - b * Hkv) * G + (r - tq_slot * G);
+  } else {
+    const int BH = B * Hq;
+    tq_slot = id / BH;
+    const int bh = id - tq_slot * BH;
+    b = bh / Hq;
+    hq = bh - b * Hq;
+  }
+  const int half = (nqt + 1) / 2;
+  const int qt = (order == ORDER_ID_ZIG && tq_slot >= half) ? tq_slot - half : nqt - 1 - tq_slot;
+  fwd_tile<D, NWG, KSPLIT, CAUSAL, FP8>(static_cast<const uint8_t*>(Qv), static_cast<const uint8_t*>(Kv),
+                                        static_cast<const uint8_t*>(Vv), O, LSE, kv_lens, B, Hq, Hkv, Tq, Tk, c,
+                                        negq, oscale, smem, b, hq, hq / G, qt);
+}
+
 template <int D, int NWG, int KSPLIT, bool CAUSAL, bool FP8>
 hipError_t launch(const FwdArgs& a, hipStream_t st, int zig_choice) {
   using C = FwdCfg<D, NWG, KSPLIT, FP8>;
@@ -775,16 +902,24 @@ hipError_t launch(const FwdArgs& a, hipStream_t st, int zig_choice) {
   const double qk = FP8 ? (double)a.scale * a.q_scale * a.k_scale : (double)a.scale;
   const float c = fmaxf((float)(fabs(qk) * 1.4426950408889634), 1e-30f);
   const int negq = qk < 0.0 ? 1 : 0;
-  // built-in zig-zag rule: at D=64 both shapes fit two workgroups per CU
-  // (64 KiB of LDS, at most 128 registers per lane), so a grid of at most
-  // two per CU is resident at once; at D=128 one per CU is, and
-  // heavy-first order is kept.  The launch table may force it either way.
-  const int zig = zig_choice >= 0 ? zig_choice
-                                  : ((CAUSAL && D == 64 && grid <= 2LL * device_cu_count()) ? 1 : 0);
-  // unit order per XCD (see the kernel) once the grid takes several rounds
-  const int uorder = (!zig && (a.B * a.Hkv) % 8 == 0 && grid >= 4LL * device_cu_count()) ? 1 : 0;
+  // Order of the tiles (see the kernel).  Zig-zag by the built-in rule: at
+  // D=64 both shapes fit two workgroups per CU (64 KiB of LDS, at most 128
+  // registers per lane), so a causal grid of at most two per CU is resident
+  // at once and pairs long and short tiles on each CU; at D=128 one per CU
+  // is, and heavy-first order is kept.  The launch table may force zig-zag
+  // either way.  Ragged grids of up to kOrderMaxB sequences otherwise run
+  // in list order (most work first, tiles with none last); other grids of
+  // several rounds take whole (batch, KV head) units per XCD when their
+  // count is a multiple of 8.
+  int order;
+  if (zig_choice == 1 || (zig_choice < 0 && CAUSAL && D == 64 && grid <= 2LL * device_cu_count()))
+    order = ORDER_ID_ZIG;
+  else if (a.kv_lens != nullptr && a.B <= kOrderMaxB)
+    order = ORDER_ID_LIST;
+  else
+    order = ((a.B * a.Hkv) % 8 == 0 && grid >= 4LL * device_cu_count()) ? ORDER_ID_UNITS : ORDER_ID_NATURAL;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NWG, KSPLIT, CAUSAL, FP8>), dim3((unsigned)grid), dim3(C::NT), 0, st, a.q,
-                     a.k, a.v, (u16*)a.o, a.lse, a.kv_lens, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, zig, uorder,
+                     a.k, a.v, (u16*)a.o, a.lse, a.kv_lens, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, negq, order,
                      FP8 ? a.v_scale : 1.f);
   return hipGetLastError();
 }
