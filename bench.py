@@ -405,7 +405,7 @@ def setup_decode_paged(torch, page_size):
         ea.attn_decode_paged(*args, torch.cuda.current_stream().cuda_stream)
 
     return dict(w=w, W=W, step=step, bytes=decode_bytes(W, w["lens"]), keep=(q, kp, vp, bt, kv, o, lse, ws),
-                out=(o, lse))
+                out=(o, lse), pages=(kp, vp, bt))
 
 
 def check_graph_replay(torch, runner, step, out):
@@ -685,7 +685,11 @@ def decode_errors(dec, n_seq=3):
     o, lse = dec["out"]
     lens = w["lens"]
     pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), W.B // 2})[:n_seq]
-    if W.dtype == "e4m3":
+    if "pages" in dec:
+        kp, vp, bt = dec["pages"]
+        ob, lb = oracle.decode_paged(w["q"].cpu(), kp, vp, bt.cpu(), lens, W.scale, batches=pick)
+        o_ref, l_ref = ob[pick], lb[pick]
+    elif W.dtype == "e4m3":
         o_ref = np.zeros((len(pick), W.Hq, W.D))
         l_ref = np.zeros((len(pick), W.Hq))
         for n, b in enumerate(pick):
@@ -742,8 +746,7 @@ def decode_entry(torch, name, steps, warmup, calls, args):
                            frac=round(achieved / PEAK_HBM_GBS, 4),
                            traffic=None if paged else traffic_for("decode_split_kernel", name),
                            kernels="decode_split + decode_merge", kernel_ms=round(ev_ms, 5)))
-    if not paged:
-        e["parity"] = decode_errors(dec)
+    e["parity"] = decode_errors(dec)
     if not args.no_cpu_baseline and not paged:
         e["cpu_baseline"] = cpu_baseline_decode(dec, args.cpu_budget)
     del runner, dec
@@ -833,7 +836,8 @@ def main():
         metric = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
     from exact_tiled_attention_13_amd import workloads as wl
 
-    W = wl.WORKLOADS[name]
+    # the paged decode runs the decode workload through a block table
+    W = wl.WORKLOADS["decode" if name == "decode-paged" else name]
     line = dict(metric=metric, value=head["value"], unit=head["unit"], n_gpus=1, steps=head["steps"],
                 warmup=head["warmup"], ms_per_step=head["ms_per_step"], higher_is_better=True, scaling="weak",
                 vs_baseline=None, dtype=head["dtype"], data="synthetic",
