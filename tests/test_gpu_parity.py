@@ -168,6 +168,60 @@ def test_long_causal_workload_two_heads_and_random_rows():
     print(f"  long workload max|dO| {max(e[0] for e in errs):.3e} max|dLSE| {max(e[1] for e in errs):.3e}")
 
 
+# ------------------------------------------------------------------ long sequences
+def test_prefill_131072_keys_sampled():
+    """Four times the long workload's length (B1 H2 T131072 D128 causal,
+    1024 query tiles per head), and a chunk of 4096 new queries at the end
+    of 131072 keys with lengths: rows at tile edges, the first and last rows
+    and random rows against the row oracle.  Offsets of a head slab reach
+    2^25 elements here."""
+    B, H, T, D = 1, 2, 131072, 128
+    q = gen((B, H, T, D), 61, torch.bfloat16)
+    k = gen((B, H, T, D), 62, torch.bfloat16)
+    v = gen((B, H, T, D), 63, torch.bfloat16)
+    sc = 1.0 / math.sqrt(D)
+    o, lse = ea.fwd(q, k, v, causal=True, scale=sc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = sorted({(0, h, i) for h in range(H) for i in (0, 1, 255, 256, 65535, 65536, T - 257, T - 256, T - 1)} |
+                  {(0, int(rng.integers(H)), int(rng.integers(T))) for _ in range(240)})
+    o_ref, l_ref = oracle.attention_rows(q.cpu(), k.cpu(), v.cpu(), rows, sc, True)
+    idx = tuple(torch.as_tensor(a, device="cuda") for a in np.array(rows).T)
+    check(o[idx], lse[idx], o_ref, l_ref, torch.bfloat16, f"prefill T{T}, {len(rows)} rows")
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    # chunked: 4096 new queries after the first Lk - 4096 of Lk keys
+    Tq, lens = 4096, [T - 1000]
+    qc = gen((B, H, Tq, D), 64, torch.bfloat16)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    workloads.poison_tail_(k, lens)
+    workloads.poison_tail_(v, lens)
+    oc, lc = ea.fwd(qc, k, v, causal=True, kv_lens=kv, scale=sc)
+    torch.cuda.synchronize()
+    rows = sorted({(0, h, i) for h in range(H) for i in (0, 255, 256, Tq - 1)} |
+                  {(0, int(rng.integers(H)), int(rng.integers(Tq))) for _ in range(120)})
+    o_ref, l_ref = oracle.attention_rows(qc.cpu(), k.cpu(), v.cpu(), rows, sc, True, lens)
+    idx = tuple(torch.as_tensor(a, device="cuda") for a in np.array(rows).T)
+    check(oc[idx], lc[idx], o_ref, l_ref, torch.bfloat16, f"chunked prefill Tq{Tq} Lk{lens[0]}, {len(rows)} rows")
+
+
+def test_decode_million_key_cache():
+    """One decode step over caches of 2^20 keys (B2 Hq8 Hkv1 D128, 2048
+    splits per sequence), one sequence full and one ragged, NaN past the
+    lengths, against the decode oracle."""
+    B, Hq, Hkv, S, D = 2, 8, 1, 1 << 20, 128
+    lens = [S, S - 333]
+    q = gen((B, Hq, D), 71, torch.bfloat16)
+    kc = gen((B, Hkv, S, D), 72, torch.bfloat16)
+    vc = gen((B, Hkv, S, D), 73, torch.bfloat16)
+    workloads.poison_tail_(kc, lens)
+    workloads.poison_tail_(vc, lens)
+    kv = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = ea.decode(q, kc, vc, kv, scale=0.09)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode(q.cpu(), kc.cpu(), vc.cpu(), lens, 0.09)
+    check(o, lse, o_ref, l_ref, torch.bfloat16, f"decode S_max {S}")
+
+
 # ------------------------------------------------------------------ edge cases
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("D", [64, 128])
