@@ -75,3 +75,39 @@ def test_noalloc_wrapper_and_size_limit():
     code = _lib.attn_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), 64, 64,
                                     8, big_S, 128, 0.1, kv.data_ptr(), _lib.MIATTN_BF16, 0, check=False)
     assert code == -7
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for: the step captured once in a HIP graph (nothing
+    allocated during capture) and replayed three times, with eager work
+    between the replays (new queries and new lengths written in place, an
+    eager decode with its own workspace), each replay bit-identical to that
+    eager decode of the same inputs."""
+    B, Hq, Hkv, S, D = 4, 16, 4, 4096, 128
+    # cache rows past the longest length any replay uses hold NaN
+    q, k, v, kv = inputs(B, Hq, Hkv, S, D, [4096, 4096, 4095, 4000], 5)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    ea.decode_noalloc(q, k, v, kv, out=out, lse=lse)   # first call on the device: scratch address
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ea.decode_noalloc(q, k, v, kv, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ea.decode_noalloc(q, k, v, kv, out=out, lse=lse)
+    gen = torch.Generator().manual_seed(9)
+    for rep, lens in enumerate(([4096, 1, 2000, 3333], [17, 4096, 4095, 512], [2048, 2048, 1, 4000])):
+        q.copy_(torch.randn(q.shape, generator=gen).to(torch.bfloat16))
+        kv.copy_(torch.tensor(lens, dtype=torch.int32))
+        o_ref, l_ref = ea.decode(q, k, v, kv)   # eager, own workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"  replay {rep}: lens {lens}", flush=True)
+        assert torch.equal(out, o_ref), f"replay {rep}: O differs from the eager decode"
+        assert torch.equal(torch.isneginf(lse), torch.isneginf(l_ref))
+        fin = torch.isfinite(l_ref)
+        assert torch.equal(lse[fin], l_ref[fin]), f"replay {rep}: LSE differs"
