@@ -72,13 +72,46 @@ __device__ __forceinline__ lds_u16* lds_base(lds_u16* p) {
   return p;
 }
 
+// HBM -> LDS copy of BYTES (16 or 4) per lane by global_load_lds from a
+// wave-uniform base plus a per-lane byte offset to the wave-uniform LDS
+// address `lds` (lane l lands at lds + BYTES l), written as inline asm (M0 =
+// the LDS address, then the load).  With an LDS DMA of the compiler builtin
+// in flight, the compiler waits for every outstanding LDS read
+// (lgkmcnt(0)) before each use of a fragment, where a count suffices; the
+// asm copies are ordered against the LDS reads by the loop's explicit vmcnt
+// waits and barriers instead.  An SALU write of M0 needs one wait state
+// before an LDS DMA reads it (not interlocked, and the hazard pass does not
+// look inside asm), hence the s_nop; M0 is declared clobbered.
+template <int BYTES>
+__device__ __forceinline__ void dma_lds(const void* gbase, uint32_t voff, const void* lds) {
+  static_assert(BYTES == 16 || BYTES == 4, "LDS DMA width");
+  // readfirstlane returns a signed int: each half is narrowed back to 32
+  // unsigned bits before widening, or a low half with bit 31 set would
+  // sign-extend into the high one
+  const uint64_t g = (uint64_t)(size_t)gbase;
+  const uint32_t ghi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint32_t glo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint8_t* gb = reinterpret_cast<const uint8_t*>(((uint64_t)ghi << 32) | (uint64_t)glo);
+  const uint32_t la = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lptr_t*)lds);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la), "v"(voff), "s"(gb)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(la), "v"(voff), "s"(gb)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
 // HBM -> LDS copy of rows [row0, row0 + ROWS) of a [rows x D] bf16 matrix
 // into a swizzled tile; each of the NWV waves issues PER 1 KiB wave-loads.
 // Rows at or past `last` are replaced by the last 16 bytes of row `last`
 // (finite data; masked).  The tile's first row is wave-uniform, so each
 // copy is addressed as that row's address plus the lane's byte offset
 // (fixed per slot), clamped by one unsigned min.
-template <int D, int ROWS, int NWV>
+// (ASM: through dma_lds, as the loop that reads the tile requires)
+template <int D, int ROWS, int NWV, bool ASM = false>
 __device__ __forceinline__ void copy_tile(const u16* src, int row0, int last, u16* dst, int w, int lane) {
   constexpr int LOADS = ROWS * D * 2 / 1024;
   constexpr int PER = (LOADS + NWV - 1) / NWV;
@@ -92,7 +125,10 @@ __device__ __forceinline__ void copy_tile(const u16* src, int row0, int last, u1
     const int r = e / D, slot = (e % D) / 8;
     const int ch = slot ^ swz<D>(r);
     const uint32_t off = (uint32_t)((r * D + ch * 8) * 2);
-    __builtin_amdgcn_global_load_lds((gptr_t*)(base + min(off, lim)), (lptr_t*)(dst + li * 512), 16, 0, 0);
+    if constexpr (ASM)
+      dma_lds<16>(base, min(off, lim), dst + li * 512);
+    else
+      __builtin_amdgcn_global_load_lds((gptr_t*)(base + min(off, lim)), (lptr_t*)(dst + li * 512), 16, 0, 0);
   }
 }
 
@@ -549,6 +585,278 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// ---------------------------------------------------------------- bwd_dkdv_pair (D = 128)
+// One pass at D = 128 without holding K, V, dK and dV in one wave: the
+// workgroup's 128 keys are four blocks of 32, each owned by a pair of waves
+// on one SIMD (waves p and p + 4).  The first wave of a pair holds the K
+// fragments and dV: it computes S = Q K^T and P for query step u, hands P
+// (fp32) to its partner through LDS and adds dV^T += dO^T P.  The second
+// holds the V fragments and dK and works one step behind: dP = dO V^T for
+// step u - 1, dS = P (dP - Drow) with the partner's P, dK^T += Q^T dS.  Every
+// product is computed once (S, dP, dV, dK), against S twice in two passes,
+// and each Q / dO tile is copied once per 128 keys.  The values are those of
+// the two-pass kernel: the same P, the same dS, the same accumulation order.
+// Stage of step u is read by the first waves in iteration u and by the
+// second in u + 1, so copies run NS - 2 steps ahead.
+template <bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(
+    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
+    const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
+    u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
+    int negk, int uorder) {
+  constexpr int D = 128, NW = 8, NPAIR = 4;
+  constexpr int BMQ = 32, NS = 4, PD = NS - 2, KS = D / 16, DB = D / 32, BNK = 32 * NPAIR;
+  constexpr int TILE = BMQ * D;
+  constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW;
+  constexpr int VM_PER_STEP = 2 * PER + 2;   // Q, dO tiles + Lc, Drow rows
+  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;   // u16 elements: Q, dO, then 64 Lc + 64 Drow floats
+  constexpr int PSLOT = 16 * 64;                 // floats: P of one pair, [register quad][lane][4]
+  static_assert(PER * NW == LOADS, "every wave issues the same number of copies");
+  __shared__ __attribute__((aligned(1024))) u16 smem[NS * STAGE];
+  __shared__ __attribute__((aligned(16))) float pbuf[2 * NPAIR * PSLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = w & (NPAIR - 1);
+  const bool first = w < NPAIR;   // wave-uniform: S, P, dV (else dP, dS, dK)
+  const int NU = B * Hkv;
+  const int id = blockIdx.x;
+  int kt, b, hk;
+  if (uorder) {
+    const int k = id >> 3, ul = k / nkt;
+    kt = k - ul * nkt;
+    const int u = (id & 7) + 8 * ul;
+    b = u / Hkv;
+    hk = u - b * Hkv;
+  } else {
+    kt = id / NU;
+    const int bh = id - kt * NU;
+    b = bh / Hkv;
+    hk = bh - b * Hkv;
+  }
+  const int G = Hq / Hkv;
+  int Lq, Lk;
+  valid_lengths(kv_lens, b, Tq, Tk, Lq, Lk);
+  const int off = Lk - Lq;
+  const int k0 = kt * BNK;
+  const int wkey0 = k0 + 32 * pr;
+  const int key = wkey0 + r32;
+
+  const u16* Kp = K + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+  const u16* Vp = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
+
+  int qfirst = 0, qend = 0;
+  if (k0 < Lk) {
+    qfirst = CAUSAL ? max(0, k0 - off) : 0;
+    qend = Lq;
+  }
+  const int nsteps_h = qend > qfirst ? (qend - qfirst + BMQ - 1) / BMQ : 0;
+  const int nsteps = G * nsteps_h;
+  const int qwave_first = CAUSAL ? wkey0 - off : 0;
+
+  const bool kok = key < Lk;
+  const TileOffsets<D> to(lane);
+  bf16x8 f[KS];   // K fragments (first waves) or V fragments (second), loaded below
+  const size_t krow = ((size_t)b * Hkv + hk) * (size_t)Tk + key;
+
+  auto step_rows = [&](int sidx, int& hq, int& q0) {
+    const int g = sidx / nsteps_h;
+    hq = hk * G + g;
+    q0 = qfirst + (sidx - g * nsteps_h) * BMQ;
+  };
+  auto issue = [&](int sidx, int st) {
+    int hq, q0;
+    step_rows(sidx, hq, q0);
+    const size_t qbase = ((size_t)b * Hq + hq) * (size_t)Tq;
+    u16* base = smem + st * STAGE;
+    copy_tile<D, BMQ, NW, true>(Q + qbase * D, q0, Lq - 1, base, w, lane);
+    copy_tile<D, BMQ, NW, true>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
+    const uint32_t roff = (uint32_t)min(q0 + r32, Lq - 1) * 4u;
+    dma_lds<4>(Lc + qbase, roff, base + 2 * TILE);
+    dma_lds<4>(Drow + qbase, roff, base + 2 * TILE + 128);
+  };
+
+  // Every step is computed by every pair, also one where no row sees a key
+  // of the pair (the mask makes its P zero, so it adds exact zeros): the
+  // pairs run in lockstep between barriers and one workgroup fills a CU, so
+  // skipping would save no time, and straight-line steps schedule better.
+  // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
+  auto q0_of = [&](int u) {
+    int hq, q0;
+    step_rows(u, hq, q0);
+    return q0;
+  };
+  auto needs_mask = [&](int q0) {
+    return (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
+  };
+  auto keep = [&](int q0, int r) {
+    const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+    return (i < Lq) & (key < Lk) & (!CAUSAL | (key <= i + off));
+  };
+  auto stage_of = [&](int u) { return (lds_u16*)&smem[(u % NS) * STAGE]; };
+  auto pslot_of = [&](int u) { return pbuf + ((u & 1) * NPAIR + pr) * PSLOT + 4 * lane; };
+  // The fragment reads of each product are all issued before its MFMAs
+  // (sched_barrier): left alone, the scheduler reads every fragment into
+  // the same registers, and each MFMA then waits out a whole LDS latency.
+  // product over D of one [32 x D] tile (row reads) with this wave's fragments
+  auto rows_times_frags = [&](lds_u16* tile) {
+    bf16x8 x[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      x[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(tile + to.row[ks]));
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 r = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) r = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[ks], f[ks], r, 0, 0, 0);
+    return r;
+  };
+  // acc^T += tile^T (D x 32, transposing reads) x frag (the step's 32 rows)
+  auto accumulate = [&](f32x16 (&acc)[DB], lds_u16* tile, const bf16x8 (&frag)[2]) {
+    bf16x8 x[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) x[db][sh] = tr_fragment<D>(tile, to, db, sh);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[db][sh], frag[sh], acc[db], 0, 0, 0);
+  };
+  auto store = [&](const f32x16 (&acc)[DB], u16* dst, float m) {
+    if (key >= Tk) return;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        u32x2 a;
+        a[0] = pack2_bf16(acc[db][4 * g4 + 0] * m, acc[db][4 * g4 + 1] * m);
+        a[1] = pack2_bf16(acc[db][4 * g4 + 2] * m, acc[db][4 * g4 + 3] * m);
+        *reinterpret_cast<u32x2*>(dst + krow * D + d0) = a;
+      }
+  };
+  // iteration t: this wave's copies of step t have landed and its P stores
+  // of step t - 1 are done (the wait includes lgkmcnt(0)); after the barrier
+  // the whole tile and the partner's P are visible, and the stage of step
+  // t - 2 (read by the second waves in t - 1) is free
+  auto sync = [&](int t) {
+    if (t < nsteps) wait_tile<VM_PER_STEP, PD - 1>(nsteps - 1 - t);
+    else wait_vm_lds<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + PD < nsteps) issue(t + PD, (t + PD) % NS);
+  };
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    if (p < nsteps) issue(p, p);
+  // K fragments (first waves, with the score sign) or V fragments (second),
+  // loaded after the prologue copies and waited for here with them, so that
+  // no wait of the compiler's own for these loads lands inside the loops
+  // (it cannot see the copies, and its count would wait for the prefetches)
+  row_fragments<KS>(f, first ? Kp : Vp, key, kok, h, (first && negk) ? 0x80008000u : 0u);
+  wait_vm_lds<0>();
+
+  f32x16 acc[DB];   // dV (first waves) or dK (second)
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  // The two roles run separate loops with the same waits and barriers
+  // (nsteps + 1 of them).
+  if (first) {
+    // iteration t: S = Q K^T, P = exp2(c S - Lc) to the partner, dV^T += dO^T P
+    for (int t = 0; t < nsteps; ++t) {
+      sync(t);
+      const int q0 = q0_of(t);
+      lds_u16* Qs = stage_of(t);
+      lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
+      float* pslot = pslot_of(t);
+      f32x16 s = rows_times_frags(Qs);
+      if (needs_mask(q0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = keep(q0, r) ? s[r] : kNegInf;
+      }
+      bf16x8 pf[2];
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 4 * h);
+        const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 8 + 4 * h);
+        f32x4 p4[2];
+        uint32_t pp[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float la = e < 4 ? l0[e] : l1[e - 4], lb = e < 4 ? l0[e + 1] : l1[e - 3];
+          const float p0 = fast_exp2(__builtin_fmaf(s[8 * sh + e], c, -la));
+          const float p1 = fast_exp2(__builtin_fmaf(s[8 * sh + e + 1], c, -lb));
+          p4[e >> 2][e & 3] = p0;
+          p4[e >> 2][(e & 3) + 1] = p1;
+          pp[e >> 1] = pack2_bf16(p0, p1);
+        }
+        *reinterpret_cast<f32x4*>(pslot + (2 * sh + 0) * 256) = p4[0];
+        *reinterpret_cast<f32x4*>(pslot + (2 * sh + 1) * 256) = p4[1];
+        pf[sh] = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
+      }
+      accumulate(acc, Qs + TILE, pf);
+    }
+    sync(nsteps);
+    store(acc, dV, 1.f);
+  } else {
+    // iteration t: dP = dO V^T of step t (masked, kept for the next
+    // iteration) and, with the partner's P of step t - 1, dS = P (dP - Drow)
+    // and dK^T += Q^T dS; the dP products of step t run beside the dS
+    // arithmetic of step t - 1
+    auto mask_dp = [&](int u, f32x16& dp) {
+      const int q0 = q0_of(u);
+      if (needs_mask(q0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = keep(q0, r) ? dp[r] : 0.f;
+      }
+    };
+    auto ds_dk = [&](int u, const f32x16& dp) {
+      lds_u16* Qs = stage_of(u);
+      lds_f32* Ds = (lds_f32*)(Qs + 2 * TILE) + 64;
+      const float* pslot = pslot_of(u);
+      bf16x8 dsf[2];
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 4 * h);
+        const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 8 + 4 * h);
+        const f32x4 pa = *reinterpret_cast<const f32x4*>(pslot + (2 * sh + 0) * 256);
+        const f32x4 pb = *reinterpret_cast<const f32x4*>(pslot + (2 * sh + 1) * 256);
+        uint32_t pd[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = e < 4 ? pa[e] : pb[e - 4], p1 = e < 4 ? pa[e + 1] : pb[e - 3];
+          const float da = e < 4 ? d0[e] : d1[e - 4], dbv = e < 4 ? d0[e + 1] : d1[e - 3];
+          pd[e >> 1] = pack2_bf16(p0 * (dp[8 * sh + e] - da), p1 * (dp[8 * sh + e + 1] - dbv));
+        }
+        dsf[sh] = __builtin_bit_cast(bf16x8, u32x4{pd[0], pd[1], pd[2], pd[3]});
+      }
+      accumulate(acc, Qs, dsf);
+    };
+    sync(0);
+    f32x16 dpp = f32x16{};   // dP of step t - 1
+    if (nsteps > 0) {
+      dpp = rows_times_frags(stage_of(0) + TILE);
+      mask_dp(0, dpp);
+    }
+    for (int t = 1; t < nsteps; ++t) {
+      sync(t);
+      f32x16 dpn = rows_times_frags(stage_of(t) + TILE);
+      ds_dk(t - 1, dpp);
+      mask_dp(t, dpn);
+      dpp = dpn;
+    }
+    if (nsteps > 0) {
+      sync(nsteps);
+      ds_dk(nsteps - 1, dpp);
+    }
+    store(acc, dK, scale);
+  }
+}
+
 constexpr int kDqWaves = 4;
 constexpr int kDkdvWaves = 4;
 
@@ -582,7 +890,14 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if constexpr (D == 128) {
+    const int nkt = (a.Tk + 127) / 128;
+    const long long grid = (long long)nkt * a.B * a.Hkv;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<CAUSAL>), dim3((unsigned)grid), dim3(512), 0, st, (const u16*)a.q,
+                       (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens, (u16*)a.dk,
+                       (u16*)a.dv, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nkt, c, a.scale, negk, uorder(grid));
+  } else {
     const int nkt = (a.Tk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
     const long long grid = (long long)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
