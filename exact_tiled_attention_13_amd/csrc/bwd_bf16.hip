@@ -18,20 +18,24 @@
 //              value tiles stream through LDS; S^T = K Q^T and dP^T = V dO^T
 //              (Q and dO fragments in registers), dS^T elementwise, then
 //              dQ^T += K^T dS^T with K^T from transposing LDS reads.
-//   bwd_dkdv   one workgroup per (batch, KV head, 32*NW keys), a lane owns a
-//              key: the query heads of the group and their query tiles
-//              stream through LDS; S = Q K^T and dP = dO V^T (K and V
+//   bwd_dkdv   (D = 64) one workgroup per (batch, KV head, 32*NW keys), a
+//              lane owns a key: the query heads of the group and their query
+//              tiles stream through LDS; S = Q K^T and dP = dO V^T (K and V
 //              fragments in registers), then dV^T += dO^T P and
 //              dK^T += Q^T dS with dO^T, Q^T from transposing LDS reads.
+//   bwd_dkdv_pair  (D = 128) the same per 128 keys, each block of 32 keys
+//              owned by a pair of waves: one computes S, P and dV, the
+//              other, one step behind, dP, dS and dK with its partner's P
+//              (handed over through LDS).
 // dQ, dK and dV are each complete inside one workgroup, so nothing is
-// accumulated through memory.
+// accumulated through memory.  HBM -> LDS copies are inline-asm LDS DMA
+// (dma_lds), and the fragment reads of each product are issued ahead of
+// its MFMAs.
 //
 // LDS tiles are row-major and unpadded with the 16-byte chunks of row r
 // XOR-ed by swz(r), chosen so that both read patterns on the same tile are
 // free of bank conflicts: 16-byte reads of 16 consecutive rows (one chunk
 // each) and transposing 8-byte reads of 4 rows x 4 chunks per 32 lanes.
-#include <type_traits>
-
 #include "device_common.h"
 #include "launch.h"
 
@@ -305,12 +309,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
 
   auto issue = [&](int t, int st) {
-    copy_tile<D, BN, NW>(Kp, t * BN, Lk - 1, smem + (st * 2 + 0) * TILE, w, lane);
-    copy_tile<D, BN, NW>(Vp, t * BN, Lk - 1, smem + (st * 2 + 1) * TILE, w, lane);
+    copy_tile<D, BN, NW, true>(Kp, t * BN, Lk - 1, smem + (st * 2 + 0) * TILE, w, lane);
+    copy_tile<D, BN, NW, true>(Vp, t * BN, Lk - 1, smem + (st * 2 + 1) * TILE, w, lane);
   };
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
     if (p < ntiles) issue(p, p);
+  // the fragment, Lc and Drow loads land here with the prologue copies, so
+  // that no wait of the compiler's own for them (which cannot count the
+  // asm copies) lands inside the loop
+  wait_vm_lds<0>();
   for (int t = 0; t < ntiles; ++t) {
     const int st = t % NS;
     wait_tile<VM_PER_TILE, NS - 2>(ntiles - 1 - t);
@@ -320,15 +328,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (kbase > kmax) continue;   // wave-uniform
     lds_u16* Ks = (lds_u16*)&smem[(st * 2 + 0) * TILE];
     lds_u16* Vs = (lds_u16*)&smem[(st * 2 + 1) * TILE];
-    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries)
+    // S^T = K Q^T and dP^T = V dO^T (32 keys x 32 queries).  The K fragment
+    // reads are issued before the score MFMAs and each V fragment read right
+    // after the MFMA that frees a K fragment's registers (pinned with
+    // scheduling barriers: left alone, the scheduler reads each fragment
+    // into the same registers just before its MFMA, which then waits out a
+    // whole LDS latency); the K^T reads of dQ are issued before the mask and
+    // the softmax arithmetic, which hide their latency.
+    bf16x8 x[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) x[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Ks + to.row[ks]));
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ka = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Ks + to.row[ks]));
-      const bf16x8 va = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Vs + to.row[ks]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[ks], qf[ks], s, 0, 0, 0);
+      x[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Vs + to.row[ks]));
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // the MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // then the read
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[ks], gf[ks], dp, 0, 0, 0);
+    bf16x8 kt[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) kt[db][sh] = tr_fragment<D>(Ks, to, db, sh);
+    __builtin_amdgcn_sched_barrier(0);
     if (kbase + BN - 1 > kfull) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -354,7 +381,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Ks, to, db, sh), dsf[sh], dq[db], 0, 0, 0);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[db][sh], dsf[sh], dq[db], 0, 0, 0);
   }
   wait_vm_lds<0>();
 
@@ -372,26 +399,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-// ---------------------------------------------------------------- bwd_dkdv
-// At D=128 one pass would hold the K and V fragments and the dK and dV
-// accumulators (192 registers per lane) plus the step's scores and
-// addresses: past 256 VGPRs, where the compiler parks the accumulators in
-// AccVGPRs and copies all 128 of them both ways on every step.  So D=128
-// runs two passes over the query tiles: first S, P and dV, then S, dP, dS
-// and dK (S is computed twice, 25% more matrix work), each pass holding 64
-// accumulators, which fits two waves per SIMD.  D=64 runs both in one pass.
-template <int D, int NW, bool CAUSAL>
+// ---------------------------------------------------------------- bwd_dkdv (D = 64)
+// One wave per 32 keys holds the K and V fragments and the dK and dV
+// accumulators (96 registers per lane at D = 64) and runs S, dP, dV and dK
+// for every query step.  (At D = 128 that is 192 registers, past what two
+// waves per SIMD allow; bwd_dkdv_pair splits the step over two waves.)
+template <int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
     int negk, int uorder) {
+  constexpr int D = 64;
   constexpr int BMQ = 32, NS = 3, KS = D / 16, DB = D / 32, BNK = 32 * NW;
   constexpr int TILE = BMQ * D;
   constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW;
   constexpr int VM_PER_STEP = 2 * PER + 2;   // Q, dO tiles + Lc, Drow rows
   constexpr int STAGE = 2 * TILE + 2 * 64 * 2;   // u16 elements: Q, dO, then 64 Lc + 64 Drow floats
-  constexpr bool SPLIT = D == 128;
+  static_assert(PER * NW == LOADS, "every wave issues the same number of copies");
   __shared__ __attribute__((aligned(1024))) u16 smem[NS * STAGE];
 
   const int tid = threadIdx.x;
@@ -436,10 +461,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int nsteps = G * nsteps_h;
   const int qwave_first = CAUSAL ? wkey0 - off : 0;   // first row that sees this wave's first key
 
-  // K fragments of this lane's key (B operand of S = Q K^T)
-  bf16x8 kf[KS];
   const bool kok = key < Lk;
-  row_fragments<KS>(kf, Kp, key, kok, h, negk ? 0x80008000u : 0u);
   const TileOffsets<D> to(lane);
   const size_t krow = ((size_t)b * Hkv + hk) * (size_t)Tk + key;
 
@@ -455,133 +477,125 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     u16* base = smem + st * STAGE;
     // rows at or past Lq (padding; may hold anything) are replaced by data
     // of row Lq - 1, and the mask below gives them no weight
-    copy_tile<D, BMQ, NW>(Q + qbase * D, q0, Lq - 1, base, w, lane);
-    copy_tile<D, BMQ, NW>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
-    const int row = min(q0 + r32, Lq - 1);
-    __builtin_amdgcn_global_load_lds((gptr_t*)(Lc + qbase + row), (lptr_t*)(base + 2 * TILE), 4, 0, 0);
-    __builtin_amdgcn_global_load_lds((gptr_t*)(Drow + qbase + row), (lptr_t*)(base + 2 * TILE + 128), 4, 0, 0);
+    copy_tile<D, BMQ, NW, true>(Q + qbase * D, q0, Lq - 1, base, w, lane);
+    copy_tile<D, BMQ, NW, true>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
+    const uint32_t roff = (uint32_t)min(q0 + r32, Lq - 1) * 4u;
+    dma_lds<4>(Lc + qbase, roff, base + 2 * TILE);
+    dma_lds<4>(Drow + qbase, roff, base + 2 * TILE + 128);
   };
 
-  // One pass over the query tiles.  PASS 0: dV only; 1: dK only; 2: both.
-  auto run = [&](auto PASSC) {
-    constexpr int PASS = decltype(PASSC)::value;
-    constexpr bool DO_V = PASS != 1, DO_K = PASS != 0;
-    // V fragments of this lane's key (B operand of dP = dO V^T)
-    bf16x8 vf[DO_K ? KS : 1];
-    if constexpr (DO_K) row_fragments<KS>(vf, Vp, key, kok, h, 0u);
-    f32x16 dk[DO_K ? DB : 1], dv[DO_V ? DB : 1];
 #pragma unroll
-    for (int i = 0; i < DB; ++i) {
-      if constexpr (DO_K) dk[i] = f32x16{};
-      if constexpr (DO_V) dv[i] = f32x16{};
-    }
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nsteps) issue(p, p);
+  // K fragments (B operand of S = Q K^T, with the score sign) and V
+  // fragments (of dP = dO V^T) of this lane's key, loaded after the prologue
+  // copies and waited for with them, so that no wait of the compiler's own
+  // for these loads (which cannot count the asm copies) lands in the loop
+  bf16x8 kf[KS], vf[KS];
+  row_fragments<KS>(kf, Kp, key, kok, h, negk ? 0x80008000u : 0u);
+  row_fragments<KS>(vf, Vp, key, kok, h, 0u);
+  wait_vm_lds<0>();
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dk[i] = dv[i] = f32x16{};
 
+  for (int sidx = 0; sidx < nsteps; ++sidx) {
+    const int st = sidx % NS;
+    wait_tile<VM_PER_STEP, NS - 2>(nsteps - 1 - sidx);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (sidx + NS - 1 < nsteps) issue(sidx + NS - 1, (sidx + NS - 1) % NS);
+    int hq, q0;
+    step_rows(sidx, hq, q0);
+    // wave-uniform: no row of this step sees a key of this wave
+    if (wkey0 >= Lk || q0 + BMQ - 1 < qwave_first) continue;
+    lds_u16* Qs = (lds_u16*)&smem[st * STAGE];
+    lds_u16* Gs = Qs + TILE;
+    lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
+    lds_f32* Ds = Ls + 64;
+    // S = Q K^T and dP = dO V^T (32 queries x 32 keys; a lane owns a key).
+    // Each product's fragment reads are issued before its MFMAs (left
+    // alone, the scheduler reads each fragment into the same registers just
+    // before its MFMA, which then waits out a whole LDS latency), and the
+    // transposing reads of dV and dK before the softmax arithmetic.
+    bf16x8 qa[KS], ga[KS];
 #pragma unroll
-    for (int p = 0; p < NS - 1; ++p)
-      if (p < nsteps) issue(p, p);
-    for (int sidx = 0; sidx < nsteps; ++sidx) {
-      const int st = sidx % NS;
-      wait_tile<VM_PER_STEP, NS - 2>(nsteps - 1 - sidx);
-      __builtin_amdgcn_s_barrier();
-      if (sidx + NS - 1 < nsteps) issue(sidx + NS - 1, (sidx + NS - 1) % NS);
-      int hq, q0;
-      step_rows(sidx, hq, q0);
-      // wave-uniform: no row of this step sees a key of this wave
-      if (wkey0 >= Lk || q0 + BMQ - 1 < qwave_first) continue;
-      lds_u16* Qs = (lds_u16*)&smem[st * STAGE];
-      lds_u16* Gs = Qs + TILE;
-      lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
-      lds_f32* Ds = Ls + 64;
-      // S = Q K^T (and dP = dO V^T) (32 queries x 32 keys; a lane owns a key)
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Qs + to.row[ks]));
+      ga[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Gs + to.row[ks]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 qa = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Qs + to.row[ks]));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
-        if constexpr (DO_K) {
-          const bf16x8 ga = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Gs + to.row[ks]));
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
-        }
-      }
-      // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
-      const bool need_mask = (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
-      if (need_mask) {
+    for (int ks = 0; ks < KS; ++ks) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], dp, 0, 0, 0);
+    }
+    bf16x8 gt[DB][2], qt[DB][2];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const bool ok = i < Lq && key < Lk && (!CAUSAL || key <= i + off);
-          s[r] = ok ? s[r] : kNegInf;
-          if constexpr (DO_K) dp[r] = ok ? dp[r] : 0.f;
-        }
-      }
-      bf16x8 pf[2], dsf[2];
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int sh = 0; sh < 2; ++sh) {
-        const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 4 * h);
-        const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 8 + 4 * h);
-        f32x4 d0{}, d1{};
-        if constexpr (DO_K) {
-          d0 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 4 * h);
-          d1 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 8 + 4 * h);
-        }
-        uint32_t pp[4], pd[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          // registers 8 sh + e, e + 1 are rows 16 sh + 8 (e >> 2) + 4 h + (e & 3), +1
-          const float la = e < 4 ? l0[e] : l1[e - 4], lb = e < 4 ? l0[e + 1] : l1[e - 3];
-          const float p0 = fast_exp2(__builtin_fmaf(s[8 * sh + e], c, -la));
-          const float p1 = fast_exp2(__builtin_fmaf(s[8 * sh + e + 1], c, -lb));
-          if constexpr (DO_V) pp[e >> 1] = pack2_bf16(p0, p1);
-          if constexpr (DO_K) {
-            const float da = e < 4 ? d0[e] : d1[e - 4], dbv = e < 4 ? d0[e + 1] : d1[e - 3];
-            pd[e >> 1] = pack2_bf16(p0 * (dp[8 * sh + e] - da), p1 * (dp[8 * sh + e + 1] - dbv));
-          }
-        }
-        if constexpr (DO_V) pf[sh] = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
-        if constexpr (DO_K) dsf[sh] = __builtin_bit_cast(bf16x8, u32x4{pd[0], pd[1], pd[2], pd[3]});
+        gt[db][sh] = tr_fragment<D>(Gs, to, db, sh);
+        qt[db][sh] = tr_fragment<D>(Qs, to, db, sh);
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (D x 32 keys)
+    __builtin_amdgcn_sched_barrier(0);
+    // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
+    const bool need_mask = (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
+    if (need_mask) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          if constexpr (DO_V)
-            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Gs, to, db, sh), pf[sh], dv[db], 0, 0, 0);
-          if constexpr (DO_K)
-            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_fragment<D>(Qs, to, db, sh), dsf[sh], dk[db], 0, 0, 0);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool ok = (i < Lq) & (key < Lk) & (!CAUSAL | (key <= i + off));
+        s[r] = ok ? s[r] : kNegInf;
+        dp[r] = ok ? dp[r] : 0.f;
+      }
     }
-    // every copy has landed and every LDS read is done; after the barrier
-    // the next pass may refill the stages
-    wait_vm_lds<0>();
-    __builtin_amdgcn_s_barrier();
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 4 * h);
+      const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 8 + 4 * h);
+      const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 4 * h);
+      const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 8 + 4 * h);
+      uint32_t pp[4], pd[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        // registers 8 sh + e, e + 1 are rows 16 sh + 8 (e >> 2) + 4 h + (e & 3), +1
+        const float la = e < 4 ? l0[e] : l1[e - 4], lb = e < 4 ? l0[e + 1] : l1[e - 3];
+        const float p0 = fast_exp2(__builtin_fmaf(s[8 * sh + e], c, -la));
+        const float p1 = fast_exp2(__builtin_fmaf(s[8 * sh + e + 1], c, -lb));
+        pp[e >> 1] = pack2_bf16(p0, p1);
+        const float da = e < 4 ? d0[e] : d1[e - 4], dbv = e < 4 ? d0[e + 1] : d1[e - 3];
+        pd[e >> 1] = pack2_bf16(p0 * (dp[8 * sh + e] - da), p1 * (dp[8 * sh + e + 1] - dbv));
+      }
+      pf[sh] = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
+      dsf[sh] = __builtin_bit_cast(bf16x8, u32x4{pd[0], pd[1], pd[2], pd[3]});
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS (D x 32 keys)
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[db][sh], pf[sh], dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db][sh], dsf[sh], dk[db], 0, 0, 0);
+      }
+  }
 
-    if (key < Tk) {
+  if (key < Tk) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d0 = 32 * db + 8 * g4 + 4 * h;
-          if constexpr (DO_K) {
-            u32x2 a;
-            a[0] = pack2_bf16(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale);
-            a[1] = pack2_bf16(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale);
-            *reinterpret_cast<u32x2*>(dK + krow * D + d0) = a;
-          }
-          if constexpr (DO_V) {
-            u32x2 v2;
-            v2[0] = pack2_bf16(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
-            v2[1] = pack2_bf16(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
-            *reinterpret_cast<u32x2*>(dV + krow * D + d0) = v2;
-          }
-        }
-    }
-  };
-  if constexpr (SPLIT) {
-    run(std::integral_constant<int, 0>{});
-    run(std::integral_constant<int, 1>{});
-  } else {
-    run(std::integral_constant<int, 2>{});
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * db + 8 * g4 + 4 * h;
+        u32x2 a, v2;
+        a[0] = pack2_bf16(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale);
+        a[1] = pack2_bf16(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale);
+        *reinterpret_cast<u32x2*>(dK + krow * D + d0) = a;
+        v2[0] = pack2_bf16(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
+        v2[1] = pack2_bf16(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
+        *reinterpret_cast<u32x2*>(dV + krow * D + d0) = v2;
+      }
   }
 }
 
@@ -901,7 +915,7 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     const int nkt = (a.Tk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
     const long long grid = (long long)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, kDkdvWaves, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDkdvWaves), 0, st,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvWaves, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDkdvWaves), 0, st,
                        (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens,
                        (u16*)a.dk, (u16*)a.dv, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nkt, c, a.scale, negk, uorder(grid));
   }
