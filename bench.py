@@ -63,7 +63,7 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h", "launch.h"],
     "bwd_prep_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
     "bwd_dq_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
-    "bwd_dkdv_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
+    "bwd_dkdv": ["bwd_bf16.hip", "device_common.h", "launch.h"],   # bwd_dkdv_kernel (D=64), bwd_dkdv_pair_kernel
     "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
     "decode_split_kernel": ["decode.hip", "device_common.h", "launch.h"],
 }
@@ -293,7 +293,7 @@ def backward_traffic(workload):
     """Scaled HBM bytes per step of the three gradient kernels from the
     committed counter summary, or None (see traffic_for)."""
     total = 0.0
-    for kn in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"):
+    for kn in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv"):
         t = traffic_for(kn, workload)
         if t is None:
             return None
