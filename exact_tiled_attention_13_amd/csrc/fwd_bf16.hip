@@ -63,6 +63,10 @@ struct FwdCfg {
   // a tile is read one iteration earlier and the ring keeps 4 stages (bf16
   // 4 x 32 KiB; E4M3 4 x 16 KiB plus the two widened V tiles)
   static constexpr bool PIPE = KSPLIT == 1 && D == 128;
+  // unpipelined D = 128 bf16 (two key groups, one workgroup per CU): the
+  // fragment reads of each product are issued ahead of its MFMAs, the V^T
+  // reads before the softmax of the tile (registers to spare)
+  static constexpr bool AHEAD = !PIPE && D == 128 && !FP8;
   static constexpr int NS = PIPE ? 4 : ((KSPLIT > 1) ? 2 : (D == 64 ? 4 : 3)) + (FP8 ? 1 : 0);
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int BM = 32 * NWG;               // query rows per workgroup
@@ -467,6 +471,23 @@ __device__ __forceinline__ void fwd_tile(
       return;
     }
     lds_u16* Ks = (lds_u16*)&ring[(st * 2 + 0) * C::TILE];
+    if constexpr (C::AHEAD) {
+      // every fragment read issued before the MFMAs (left alone, the
+      // scheduler reads each into the same registers just before its MFMA)
+      bf16x8 a[C::KS][C::KB];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        lds_u16* kp = lds_base(Ks + koff[ks]);
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) a[ks][kb] = *(const __attribute__((address_space(3))) bf16x8*)(kp + 32 * kb * D);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) sd[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][kb], qf[ks], sd[kb], 0, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       // one per-lane base per k-step; the key-block offset folds into the
@@ -616,6 +637,33 @@ __device__ __forceinline__ void fwd_tile(
     }
   };
 
+  // ---- V^T fragments of the bf16 V tile at vbase, and O^T += V^T P^T with
+  // them (AHEAD: the reads are issued before the tile's softmax)
+  auto read_v = [&](u16* vbase, bf16x8 (&vfr)[C::DB][C::KB][2]) {
+    lds_u16* Vs = (lds_u16*)vbase;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      lds_u16* vrow = lds_base(Vs + voff[db]);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          lds_u16* vp = vrow + (32 * kb + 16 * sh) * D;
+          const u32x2 lo = lds_read_tr16(vp);
+          const u32x2 hi = lds_read_tr16(vp + 8 * D);
+          vfr[db][kb][sh] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+    }
+  };
+  auto pv_from = [&](const bf16x8 (&vfr)[C::DB][C::KB][2]) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[db][kb][sh], pf[kb][sh], oacc[db], 0, 0, 0);
+  };
+
   // ---- O^T += V^T P^T with the bf16 V tile at vbase
   auto do_pv = [&](u16* vbase) {
     lds_u16* Vs = (lds_u16*)vbase;
@@ -738,6 +786,15 @@ __device__ __forceinline__ void fwd_tile(
       const int kbase = tile_of(lt) * C::BN;
       if (lt >= ntiles || kbase > kmax) continue;   // wave-uniform: nothing of this tile for the wave
       do_scores(st, s[0]);
+      if constexpr (C::AHEAD) {
+        bf16x8 vfr[C::DB][C::KB][2];
+        read_v(ring + (st * 2 + 1) * C::TILE, vfr);
+        __builtin_amdgcn_sched_barrier(0);
+        do_max(s[0], kbase);
+        do_exp(s[0]);
+        pv_from(vfr);
+        continue;
+      }
       do_max(s[0], kbase);
       do_exp(s[0]);
       if constexpr (FP8)
