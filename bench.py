@@ -860,6 +860,7 @@ def main():
         line["decode_fp8"] = decode_entry(torch, "decode-fp8", ex, 5, 20, args)
         line["prefill_fp8"] = prefill_entry(torch, "long-fp8", ex, 3, 20, args)
         line["backward"] = backward_entry(torch, "causal", 2 * ex, 5, 20, args)
+        line["backward_long"] = backward_entry(torch, "long", 5, 2, 5, args)
         line["single"] = prefill_entry(torch, "single", 10 * ex, 5, 20, args)
     print(json.dumps(line), flush=True)
 
