@@ -18,15 +18,14 @@
 //              value tiles stream through LDS; S^T = K Q^T and dP^T = V dO^T
 //              (Q and dO fragments in registers), dS^T elementwise, then
 //              dQ^T += K^T dS^T with K^T from transposing LDS reads.
-//   bwd_dkdv   (D = 64) one workgroup per (batch, KV head, 32*NW keys), a
-//              lane owns a key: the query heads of the group and their query
-//              tiles stream through LDS; S = Q K^T and dP = dO V^T (K and V
-//              fragments in registers), then dV^T += dO^T P and
-//              dK^T += Q^T dS with dO^T, Q^T from transposing LDS reads.
-//   bwd_dkdv_pair  (D = 128) the same per 128 keys, each block of 32 keys
-//              owned by a pair of waves: one computes S, P and dV, the
-//              other, one step behind, dP, dS and dK with its partner's P
-//              (handed over through LDS).
+//   bwd_dkdv_pair  one workgroup per (batch, KV head, 128 keys), a lane
+//              owns a key: the query heads of the group and their query
+//              tiles stream through LDS.  Each block of 32 keys is owned by
+//              a pair of waves: one computes S = Q K^T, P and
+//              dV^T += dO^T P, the other, one step behind, dP = dO V^T,
+//              dS and dK^T += Q^T dS with its partner's P (handed over
+//              through LDS); K and V fragments in registers, dO^T and Q^T
+//              from transposing LDS reads.
 // dQ, dK and dV are each complete inside one workgroup, so nothing is
 // accumulated through memory.  HBM -> LDS copies are inline-asm LDS DMA
 // (dma_lds), and the fragment reads of each product are issued ahead of
@@ -66,7 +65,6 @@ __device__ __forceinline__ void wait_tile(int rem) {
   }
 }
 
-typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
 typedef __attribute__((address_space(3))) const u16 lds_u16;
 typedef __attribute__((address_space(3))) const float lds_f32;
@@ -114,8 +112,7 @@ __device__ __forceinline__ void dma_lds(const void* gbase, uint32_t voff, const 
 // (finite data; masked).  The tile's first row is wave-uniform, so each
 // copy is addressed as that row's address plus the lane's byte offset
 // (fixed per slot), clamped by one unsigned min.
-// (ASM: through dma_lds, as the loop that reads the tile requires)
-template <int D, int ROWS, int NWV, bool ASM = false>
+template <int D, int ROWS, int NWV>
 __device__ __forceinline__ void copy_tile(const u16* src, int row0, int last, u16* dst, int w, int lane) {
   constexpr int LOADS = ROWS * D * 2 / 1024;
   constexpr int PER = (LOADS + NWV - 1) / NWV;
@@ -129,10 +126,7 @@ __device__ __forceinline__ void copy_tile(const u16* src, int row0, int last, u1
     const int r = e / D, slot = (e % D) / 8;
     const int ch = slot ^ swz<D>(r);
     const uint32_t off = (uint32_t)((r * D + ch * 8) * 2);
-    if constexpr (ASM)
-      dma_lds<16>(base, min(off, lim), dst + li * 512);
-    else
-      __builtin_amdgcn_global_load_lds((gptr_t*)(base + min(off, lim)), (lptr_t*)(dst + li * 512), 16, 0, 0);
+    dma_lds<16>(base, min(off, lim), dst + li * 512);
   }
 }
 
@@ -309,8 +303,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int i = 0; i < DB; ++i) dq[i] = f32x16{};
 
   auto issue = [&](int t, int st) {
-    copy_tile<D, BN, NW, true>(Kp, t * BN, Lk - 1, smem + (st * 2 + 0) * TILE, w, lane);
-    copy_tile<D, BN, NW, true>(Vp, t * BN, Lk - 1, smem + (st * 2 + 1) * TILE, w, lane);
+    copy_tile<D, BN, NW>(Kp, t * BN, Lk - 1, smem + (st * 2 + 0) * TILE, w, lane);
+    copy_tile<D, BN, NW>(Vp, t * BN, Lk - 1, smem + (st * 2 + 1) * TILE, w, lane);
   };
 #pragma unroll
   for (int p = 0; p < NS - 1; ++p)
@@ -399,233 +393,37 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-// ---------------------------------------------------------------- bwd_dkdv (D = 64)
-// One wave per 32 keys holds the K and V fragments and the dK and dV
-// accumulators (96 registers per lane at D = 64) and runs S, dP, dV and dK
-// for every query step.  (At D = 128 that is 192 registers, past what two
-// waves per SIMD allow; bwd_dkdv_pair splits the step over two waves.)
-template <int NW, bool CAUSAL>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
-    const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
-    const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
-    u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
-    int negk, int uorder) {
-  constexpr int D = 64;
-  constexpr int BMQ = 32, NS = 3, KS = D / 16, DB = D / 32, BNK = 32 * NW;
-  constexpr int TILE = BMQ * D;
-  constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW;
-  constexpr int VM_PER_STEP = 2 * PER + 2;   // Q, dO tiles + Lc, Drow rows
-  constexpr int STAGE = 2 * TILE + 2 * 64 * 2;   // u16 elements: Q, dO, then 64 Lc + 64 Drow floats
-  static_assert(PER * NW == LOADS, "every wave issues the same number of copies");
-  __shared__ __attribute__((aligned(1024))) u16 smem[NS * STAGE];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, h = lane >> 5, r32 = lane & 31;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // workgroup -> (key tile, batch, KV head); as for dQ, with uorder each
-  // XCD takes whole units, so its resident workgroups stream one unit's Q
-  // and dO through L2 together
-  const int NU = B * Hkv;
-  const int id = blockIdx.x;
-  int kt, b, hk;
-  if (uorder) {
-    const int k = id >> 3, ul = k / nkt;
-    kt = k - ul * nkt;
-    const int u = (id & 7) + 8 * ul;
-    b = u / Hkv;
-    hk = u - b * Hkv;
-  } else {
-    kt = id / NU;
-    const int bh = id - kt * NU;
-    b = bh / Hkv;
-    hk = bh - b * Hkv;
-  }
-  const int G = Hq / Hkv;
-  int Lq, Lk;
-  valid_lengths(kv_lens, b, Tq, Tk, Lq, Lk);
-  const int off = Lk - Lq;
-  const int k0 = kt * BNK;
-  const int wkey0 = k0 + 32 * w;   // this wave's keys [wkey0, wkey0 + 32)
-  const int key = wkey0 + r32;     // this lane's key
-
-  const u16* Kp = K + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
-  const u16* Vp = V + ((size_t)b * Hkv + hk) * (size_t)Tk * D;
-
-  // query rows that see any key of the workgroup / of this wave
-  int qfirst = 0, qend = 0;
-  if (k0 < Lk) {
-    qfirst = CAUSAL ? max(0, k0 - off) : 0;
-    qend = Lq;
-  }
-  const int nsteps_h = qend > qfirst ? (qend - qfirst + BMQ - 1) / BMQ : 0;
-  const int nsteps = G * nsteps_h;
-  const int qwave_first = CAUSAL ? wkey0 - off : 0;   // first row that sees this wave's first key
-
-  const bool kok = key < Lk;
-  const TileOffsets<D> to(lane);
-  const size_t krow = ((size_t)b * Hkv + hk) * (size_t)Tk + key;
-
-  auto step_rows = [&](int sidx, int& hq, int& q0) {
-    const int g = sidx / nsteps_h;
-    hq = hk * G + g;
-    q0 = qfirst + (sidx - g * nsteps_h) * BMQ;
-  };
-  auto issue = [&](int sidx, int st) {
-    int hq, q0;
-    step_rows(sidx, hq, q0);
-    const size_t qbase = ((size_t)b * Hq + hq) * (size_t)Tq;
-    u16* base = smem + st * STAGE;
-    // rows at or past Lq (padding; may hold anything) are replaced by data
-    // of row Lq - 1, and the mask below gives them no weight
-    copy_tile<D, BMQ, NW, true>(Q + qbase * D, q0, Lq - 1, base, w, lane);
-    copy_tile<D, BMQ, NW, true>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
-    const uint32_t roff = (uint32_t)min(q0 + r32, Lq - 1) * 4u;
-    dma_lds<4>(Lc + qbase, roff, base + 2 * TILE);
-    dma_lds<4>(Drow + qbase, roff, base + 2 * TILE + 128);
-  };
-
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p)
-    if (p < nsteps) issue(p, p);
-  // K fragments (B operand of S = Q K^T, with the score sign) and V
-  // fragments (of dP = dO V^T) of this lane's key, loaded after the prologue
-  // copies and waited for with them, so that no wait of the compiler's own
-  // for these loads (which cannot count the asm copies) lands in the loop
-  bf16x8 kf[KS], vf[KS];
-  row_fragments<KS>(kf, Kp, key, kok, h, negk ? 0x80008000u : 0u);
-  row_fragments<KS>(vf, Vp, key, kok, h, 0u);
-  wait_vm_lds<0>();
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) dk[i] = dv[i] = f32x16{};
-
-  for (int sidx = 0; sidx < nsteps; ++sidx) {
-    const int st = sidx % NS;
-    wait_tile<VM_PER_STEP, NS - 2>(nsteps - 1 - sidx);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (sidx + NS - 1 < nsteps) issue(sidx + NS - 1, (sidx + NS - 1) % NS);
-    int hq, q0;
-    step_rows(sidx, hq, q0);
-    // wave-uniform: no row of this step sees a key of this wave
-    if (wkey0 >= Lk || q0 + BMQ - 1 < qwave_first) continue;
-    lds_u16* Qs = (lds_u16*)&smem[st * STAGE];
-    lds_u16* Gs = Qs + TILE;
-    lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
-    lds_f32* Ds = Ls + 64;
-    // S = Q K^T and dP = dO V^T (32 queries x 32 keys; a lane owns a key).
-    // Each product's fragment reads are issued before its MFMAs (left
-    // alone, the scheduler reads each fragment into the same registers just
-    // before its MFMA, which then waits out a whole LDS latency), and the
-    // transposing reads of dV and dK before the softmax arithmetic.
-    bf16x8 qa[KS], ga[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qa[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Qs + to.row[ks]));
-      ga[ks] = *(const __attribute__((address_space(3))) bf16x8*)(lds_base(Gs + to.row[ks]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vf[ks], dp, 0, 0, 0);
-    }
-    bf16x8 gt[DB][2], qt[DB][2];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        gt[db][sh] = tr_fragment<D>(Gs, to, db, sh);
-        qt[db][sh] = tr_fragment<D>(Qs, to, db, sh);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
-    const bool need_mask = (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
-    if (need_mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = q0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool ok = (i < Lq) & (key < Lk) & (!CAUSAL | (key <= i + off));
-        s[r] = ok ? s[r] : kNegInf;
-        dp[r] = ok ? dp[r] : 0.f;
-      }
-    }
-    bf16x8 pf[2], dsf[2];
-#pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-      const f32x4 l0 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 4 * h);
-      const f32x4 l1 = *(const __attribute__((address_space(3))) f32x4*)(Ls + 16 * sh + 8 + 4 * h);
-      const f32x4 d0 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 4 * h);
-      const f32x4 d1 = *(const __attribute__((address_space(3))) f32x4*)(Ds + 16 * sh + 8 + 4 * h);
-      uint32_t pp[4], pd[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // registers 8 sh + e, e + 1 are rows 16 sh + 8 (e >> 2) + 4 h + (e & 3), +1
-        const float la = e < 4 ? l0[e] : l1[e - 4], lb = e < 4 ? l0[e + 1] : l1[e - 3];
-        const float p0 = fast_exp2(__builtin_fmaf(s[8 * sh + e], c, -la));
-        const float p1 = fast_exp2(__builtin_fmaf(s[8 * sh + e + 1], c, -lb));
-        pp[e >> 1] = pack2_bf16(p0, p1);
-        const float da = e < 4 ? d0[e] : d1[e - 4], dbv = e < 4 ? d0[e + 1] : d1[e - 3];
-        pd[e >> 1] = pack2_bf16(p0 * (dp[8 * sh + e] - da), p1 * (dp[8 * sh + e + 1] - dbv));
-      }
-      pf[sh] = __builtin_bit_cast(bf16x8, u32x4{pp[0], pp[1], pp[2], pp[3]});
-      dsf[sh] = __builtin_bit_cast(bf16x8, u32x4{pd[0], pd[1], pd[2], pd[3]});
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (D x 32 keys)
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int sh = 0; sh < 2; ++sh) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt[db][sh], pf[sh], dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt[db][sh], dsf[sh], dk[db], 0, 0, 0);
-      }
-  }
-
-  if (key < Tk) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * db + 8 * g4 + 4 * h;
-        u32x2 a, v2;
-        a[0] = pack2_bf16(dk[db][4 * g4 + 0] * scale, dk[db][4 * g4 + 1] * scale);
-        a[1] = pack2_bf16(dk[db][4 * g4 + 2] * scale, dk[db][4 * g4 + 3] * scale);
-        *reinterpret_cast<u32x2*>(dK + krow * D + d0) = a;
-        v2[0] = pack2_bf16(dv[db][4 * g4 + 0], dv[db][4 * g4 + 1]);
-        v2[1] = pack2_bf16(dv[db][4 * g4 + 2], dv[db][4 * g4 + 3]);
-        *reinterpret_cast<u32x2*>(dV + krow * D + d0) = v2;
-      }
-  }
-}
-
-// ---------------------------------------------------------------- bwd_dkdv_pair (D = 128)
-// One pass at D = 128 without holding K, V, dK and dV in one wave: the
-// workgroup's 128 keys are four blocks of 32, each owned by a pair of waves
+// ---------------------------------------------------------------- bwd_dkdv_pair
+// dK and dV without holding K, V, dK and dV in one wave (at D = 128 that is
+// past the registers of two waves per SIMD; at D = 64 the split halves each
+// wave's chain of products per step and fits 128 VGPRs, two workgroups per
+// CU): the workgroup's 128 keys are four blocks of 32, each owned by a pair of waves
 // on one SIMD (waves p and p + 4).  The first wave of a pair holds the K
 // fragments and dV: it computes S = Q K^T and P for query step u, hands P
 // (fp32) to its partner through LDS and adds dV^T += dO^T P.  The second
 // holds the V fragments and dK and works one step behind: dP = dO V^T for
 // step u - 1, dS = P (dP - Drow) with the partner's P, dK^T += Q^T dS.  Every
-// product is computed once (S, dP, dV, dK), against S twice in two passes,
-// and each Q / dO tile is copied once per 128 keys.  The values are those of
-// the two-pass kernel: the same P, the same dS, the same accumulation order.
+// product is computed once (S, dP, dV, dK) and each Q / dO tile is copied
+// once per 128 keys.
 // Stage of step u is read by the first waves in iteration u and by the
 // second in u + 1, so copies run NS - 2 steps ahead.
-template <bool CAUSAL>
-__global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void bwd_dkdv_pair_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dK, u16* __restrict__ dV, int B, int Hq, int Hkv, int Tq, int Tk, int nkt, float c, float scale,
     int negk, int uorder) {
-  constexpr int D = 128, NW = 8, NPAIR = 4;
+  constexpr int NW = 8, NPAIR = 4;
   constexpr int BMQ = 32, NS = 4, PD = NS - 2, KS = D / 16, DB = D / 32, BNK = 32 * NPAIR;
   constexpr int TILE = BMQ * D;
-  constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW;
-  constexpr int VM_PER_STEP = 2 * PER + 2;   // Q, dO tiles + Lc, Drow rows
+  // the Q and dO tiles are 2 LOADS wave-loads of 1 KiB, PER per wave (at
+  // D = 64 waves 0-3 copy Q and waves 4-7 dO)
+  constexpr int LOADS = TILE * 2 / 1024, PER = 2 * LOADS / NW;
+  constexpr int VM_PER_STEP = PER + 2;   // Q, dO tiles + Lc, Drow rows
   constexpr int STAGE = 2 * TILE + 2 * 64 * 2;   // u16 elements: Q, dO, then 64 Lc + 64 Drow floats
   constexpr int PSLOT = 16 * 64;                 // floats: P of one pair, [register quad][lane][4]
-  static_assert(PER * NW == LOADS, "every wave issues the same number of copies");
+  static_assert(D == 64 || D == 128, "head dimension");
+  static_assert(PER * NW == 2 * LOADS, "every wave issues the same number of copies");
   __shared__ __attribute__((aligned(1024))) u16 smem[NS * STAGE];
   __shared__ __attribute__((aligned(16))) float pbuf[2 * NPAIR * PSLOT];
 
@@ -684,8 +482,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(
     step_rows(sidx, hq, q0);
     const size_t qbase = ((size_t)b * Hq + hq) * (size_t)Tq;
     u16* base = smem + st * STAGE;
-    copy_tile<D, BMQ, NW, true>(Q + qbase * D, q0, Lq - 1, base, w, lane);
-    copy_tile<D, BMQ, NW, true>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
+    if constexpr (D == 128) {
+      copy_tile<D, BMQ, NW>(Q + qbase * D, q0, Lq - 1, base, w, lane);
+      copy_tile<D, BMQ, NW>(dO + qbase * D, q0, Lq - 1, base + TILE, w, lane);
+    } else {
+      const bool q_half = w < NW / 2;   // wave-uniform
+      copy_tile<D, BMQ, NW / 2>((q_half ? Q : dO) + qbase * D, q0, Lq - 1, base + (q_half ? 0 : TILE),
+                                      w & (NW / 2 - 1), lane);
+    }
     const uint32_t roff = (uint32_t)min(q0 + r32, Lq - 1) * 4u;
     dma_lds<4>(Lc + qbase, roff, base + 2 * TILE);
     dma_lds<4>(Drow + qbase, roff, base + 2 * TILE + 128);
@@ -850,29 +654,40 @@ __global__ __launch_bounds__(512) void bwd_dkdv_pair_kernel(
       }
       accumulate(acc, Qs, dsf);
     };
-    sync(0);
-    f32x16 dpp = f32x16{};   // dP of step t - 1
-    if (nsteps > 0) {
-      dpp = rows_times_frags(stage_of(0) + TILE);
-      mask_dp(0, dpp);
-    }
-    for (int t = 1; t < nsteps; ++t) {
-      sync(t);
-      f32x16 dpn = rows_times_frags(stage_of(t) + TILE);
-      ds_dk(t - 1, dpp);
-      mask_dp(t, dpn);
-      dpp = dpn;
-    }
-    if (nsteps > 0) {
-      sync(nsteps);
-      ds_dk(nsteps - 1, dpp);
+    if constexpr (D == 128) {
+      sync(0);
+      f32x16 dpp = f32x16{};   // dP of step t - 1
+      if (nsteps > 0) {
+        dpp = rows_times_frags(stage_of(0) + TILE);
+        mask_dp(0, dpp);
+      }
+      for (int t = 1; t < nsteps; ++t) {
+        sync(t);
+        f32x16 dpn = rows_times_frags(stage_of(t) + TILE);
+        ds_dk(t - 1, dpp);
+        mask_dp(t, dpn);
+        dpp = dpn;
+      }
+      if (nsteps > 0) {
+        sync(nsteps);
+        ds_dk(nsteps - 1, dpp);
+      }
+    } else {
+      // (D = 64: the chains are short and two dP tiles in flight would not
+      // fit 128 registers, so iteration t computes dP, dS and dK of step t - 1)
+      sync(0);
+      for (int t = 1; t <= nsteps; ++t) {
+        sync(t);
+        f32x16 dp = rows_times_frags(stage_of(t - 1) + TILE);
+        mask_dp(t - 1, dp);
+        ds_dk(t - 1, dp);
+      }
     }
     store(acc, dK, scale);
   }
 }
 
 constexpr int kDqWaves = 4;
-constexpr int kDkdvWaves = 4;
 
 template <int D, bool CAUSAL>
 hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
@@ -904,20 +719,13 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if constexpr (D == 128) {
+  {
     const int nkt = (a.Tk + 127) / 128;
     const long long grid = (long long)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<CAUSAL>), dim3((unsigned)grid), dim3(512), 0, st, (const u16*)a.q,
+    hipLaunchKernelGGL((bwd_dkdv_pair_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(512), 0, st, (const u16*)a.q,
                        (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens, (u16*)a.dk,
                        (u16*)a.dv, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nkt, c, a.scale, negk, uorder(grid));
-  } else {
-    const int nkt = (a.Tk + 32 * kDkdvWaves - 1) / (32 * kDkdvWaves);
-    const long long grid = (long long)nkt * a.B * a.Hkv;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<kDkdvWaves, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDkdvWaves), 0, st,
-                       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens,
-                       (u16*)a.dk, (u16*)a.dv, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nkt, c, a.scale, negk, uorder(grid));
   }
   return hipGetLastError();
 }
