@@ -63,7 +63,7 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h", "launch.h"],
     "bwd_prep_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
     "bwd_dq_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
-    "bwd_dkdv": ["bwd_bf16.hip", "device_common.h", "launch.h"],   # bwd_dkdv_kernel (D=64), bwd_dkdv_pair_kernel
+    "bwd_dkdv": ["bwd_bf16.hip", "device_common.h", "launch.h"],   # bwd_dkdv_pair_kernel
     "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
     "decode_split_kernel": ["decode.hip", "device_common.h", "launch.h"],
 }
