@@ -115,6 +115,14 @@ def blas_threads():
         return os.cpu_count() or 1
 
 
+def host_cores():
+    """CPU cores this process may run on (the BLAS threads are reported as `cores`)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 class Graphed:
     """A HIP graph holding `calls` calls of fn, replayed to run steps."""
 
@@ -324,7 +332,8 @@ def cpu_baseline_backward(name, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return dict(value=done / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+    return dict(value=done / dt / 1e12, unit="TFLOP/s", cores=blas_threads(),
+                host_cores=host_cores(), kind="oracle",
                 sample=f"gradients of {heads} of {W.B * W.Hq} (batch, head) pairs of the {W.name} workload, "
                        f"float64 numpy, {dt:.1f} s")
 
@@ -448,7 +457,8 @@ def cpu_baseline_prefill(name, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return dict(value=done_flops / dt / 1e12, unit="TFLOP/s", cores=blas_threads(), kind="oracle",
+    return dict(value=done_flops / dt / 1e12, unit="TFLOP/s", cores=blas_threads(),
+                host_cores=host_cores(), kind="oracle",
                 sample=f"{heads} of {W.B * W.Hq} (batch, head) pairs of the {W.name} workload, float64 numpy, "
                        f"{dt:.1f} s")
 
@@ -475,7 +485,8 @@ def cpu_baseline_decode(dec, budget_s):
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return dict(value=done / dt / 1e9, unit="GB/s", cores=blas_threads(), kind="oracle",
+    return dict(value=done / dt / 1e9, unit="GB/s", cores=blas_threads(),
+                host_cores=host_cores(), kind="oracle",
                 sample=f"{nb} of {W.B} sequences of the {W.name} workload (cache slabs upcast to float64), "
                        f"{dt:.1f} s")
 
