@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
     u16* __restrict__ dQ, int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, float scale, int negk,
     int uorder) {
-  constexpr int BN = 32, NS = 3, KS = D / 16, DB = D / 32, BM = 32 * NW;
+  constexpr int BN = 32, NS = 4, KS = D / 16, DB = D / 32, BM = 32 * NW;
   constexpr int TILE = BN * D;
   constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW, VM_PER_TILE = 2 * PER;
   __shared__ __attribute__((aligned(1024))) u16 smem[NS * 2 * TILE];   // [stage][K, V][tile]
