@@ -495,16 +495,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     dma_lds<4>(Drow + qbase, roff, base + 2 * TILE + 128);
   };
 
-  // Every step is computed by every pair, also one where no row sees a key
-  // of the pair (the mask makes its P zero, so it adds exact zeros): the
-  // pairs run in lockstep between barriers and one workgroup fills a CU, so
-  // skipping would save no time, and straight-line steps schedule better.
+  // At D = 128 every step is computed by every pair, also one where no row
+  // sees a key of the pair (the mask makes its P zero, so it adds exact
+  // zeros): the pairs run in lockstep between barriers and one workgroup
+  // fills a CU, so skipping would save no time, and straight-line steps
+  // schedule better.
   // register r holds query row q0 + 8 (r >> 2) + 4 h + (r & 3)
   auto q0_of = [&](int u) {
     int hq, q0;
     step_rows(u, hq, q0);
     return q0;
   };
+  // (D = 64: a step where no row sees a key of the pair is skipped by both
+  // of its waves, which frees their SIMD for the CU's other workgroup)
+  auto skips = [&](int q0) { return wkey0 >= Lk || q0 + BMQ - 1 < qwave_first; };
   auto needs_mask = [&](int q0) {
     return (q0 + BMQ > Lq) || (wkey0 + 31 >= Lk) || (CAUSAL && wkey0 + 31 > q0 + off);
   };
@@ -588,6 +592,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
     for (int t = 0; t < nsteps; ++t) {
       sync(t);
       const int q0 = q0_of(t);
+      if constexpr (D == 64)
+        if (skips(q0)) continue;
       lds_u16* Qs = stage_of(t);
       lds_f32* Ls = (lds_f32*)(Qs + 2 * TILE);
       float* pslot = pslot_of(t);
@@ -678,6 +684,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4
       sync(0);
       for (int t = 1; t <= nsteps; ++t) {
         sync(t);
+        if (skips(q0_of(t - 1))) continue;
         f32x16 dp = rows_times_frags(stage_of(t - 1) + TILE);
         mask_dp(t - 1, dp);
         ds_dk(t - 1, dp);
