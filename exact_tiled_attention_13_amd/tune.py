@@ -151,19 +151,35 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=tiles.DEFAULT_PATH)
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--only", default=None, metavar="OP,DTYPE,D",
+                    help="re-tune only these keys (e.g. fwd,bf16,128) and keep the other entries of --out")
     args = ap.parse_args(argv)
     if not torch.cuda.is_available():
         sys.exit("the tuner needs a GPU")
+    only = None
+    if args.only:
+        op, dt, d = args.only.split(",")
+        if op not in ("fwd", "decode") or dt not in ("bf16", "e4m3") or d not in ("64", "128"):
+            sys.exit(f"--only {args.only}: expected fwd|decode,bf16|e4m3,64|128")
+        only = (op, dt, int(d))
     _lib.load()
     entries = []
     try:
         for dtype in ("bf16", "e4m3"):
             for D in (64, 128):
-                for causal in (0, 1):
-                    entries += tune_fwd(dtype, D, causal, args.reps)
-                entries += tune_decode(dtype, D, args.reps)
+                if only is None or only == ("fwd", dtype, D):
+                    for causal in (0, 1):
+                        entries += tune_fwd(dtype, D, causal, args.reps)
+                if only is None or only == ("decode", dtype, D):
+                    entries += tune_decode(dtype, D, args.reps)
     finally:
         _lib.attn_set_tile_table([])
+    if only is not None:
+        # keep the other keys' entries, in the table's order
+        with open(args.out) as fh:
+            old = json.load(fh)["entries"]
+        keep = [e for e in old if (e["op"], e["dtype"], e["D"]) != only]
+        entries = keep + entries
     doc = dict(arch="gfx950", device=torch.cuda.get_device_name(0), fields=tiles.FIELDS,
                note="written by python -m exact_tiled_attention_13_amd.tune; times in ms per call",
                entries=entries)
