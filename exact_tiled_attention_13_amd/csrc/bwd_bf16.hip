@@ -397,16 +397,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // dK and dV without holding K, V, dK and dV in one wave (at D = 128 that is
 // past the registers of two waves per SIMD; at D = 64 the split halves each
 // wave's chain of products per step and fits 128 VGPRs, two workgroups per
-// CU): the workgroup's 128 keys are four blocks of 32, each owned by a pair of waves
-// on one SIMD (waves p and p + 4).  The first wave of a pair holds the K
-// fragments and dV: it computes S = Q K^T and P for query step u, hands P
-// (fp32) to its partner through LDS and adds dV^T += dO^T P.  The second
-// holds the V fragments and dK and works one step behind: dP = dO V^T for
-// step u - 1, dS = P (dP - Drow) with the partner's P, dK^T += Q^T dS.  Every
-// product is computed once (S, dP, dV, dK) and each Q / dO tile is copied
-// once per 128 keys.
-// Stage of step u is read by the first waves in iteration u and by the
-// second in u + 1, so copies run NS - 2 steps ahead.
+// CU).  The workgroup's 128 keys are four blocks of 32, each owned by a pair
+// of waves on one SIMD (waves p and p + 4).  The first wave of a pair holds
+// the K fragments and dV: in iteration u it computes S = Q K^T and P of
+// query step u, hands P (fp32) to its partner through LDS and adds
+// dV^T += dO^T P.  The second holds the V fragments and dK and finishes step
+// u in iteration u + 1: dS = P (dP - Drow) with the partner's P and
+// dK^T += Q^T dS, with dP = dO V^T of step u computed in iteration u beside
+// the previous step's arithmetic (D = 128) or in iteration u + 1 (D = 64).
+// Every product is computed once (S, dP, dV, dK) and each Q / dO tile is
+// copied once per 128 keys.  The stage of step u is read in iterations u
+// and u + 1, so copies run NS - 2 steps ahead.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(D == 64 ? 4 : 2))) void bwd_dkdv_pair_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
