@@ -147,6 +147,16 @@ def tune_decode(dtype, D, reps):
     return entries
 
 
+def merge_only(old, new, only):
+    """The entries of a table re-tuned for one (op, dtype, D): `old`'s
+    entries of the other keys, in their order, then `new` (whose entries
+    must all carry that key).  Keys of different (op, dtype, D) never match
+    the same call, so their order does not matter."""
+    if any((e["op"], e["dtype"], e["D"]) != tuple(only) for e in new):
+        raise ValueError(f"re-tuned entries outside {only}")
+    return [e for e in old if (e["op"], e["dtype"], e["D"]) != tuple(only)] + list(new)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=tiles.DEFAULT_PATH)
@@ -175,11 +185,8 @@ def main(argv=None):
     finally:
         _lib.attn_set_tile_table([])
     if only is not None:
-        # keep the other keys' entries, in the table's order
         with open(args.out) as fh:
-            old = json.load(fh)["entries"]
-        keep = [e for e in old if (e["op"], e["dtype"], e["D"]) != only]
-        entries = keep + entries
+            entries = merge_only(json.load(fh)["entries"], entries, only)
     doc = dict(arch="gfx950", device=torch.cuda.get_device_name(0), fields=tiles.FIELDS,
                note="written by python -m exact_tiled_attention_13_amd.tune; times in ms per call",
                entries=entries)

@@ -171,3 +171,25 @@ def test_bad_json_is_refused(tmp_path):
         tiles.entries_from_json({"entries": [{"op": "fwd"}]})
     with pytest.raises(ValueError):
         tiles.entries_from_json([])
+
+
+def test_tuner_merge_keeps_other_keys():
+    """`tune --only OP,DTYPE,D` re-measures one key set and keeps the rest of
+    the table: every entry of the other keys survives unchanged, the old
+    entries of the re-tuned key are replaced, and the merged document loads."""
+    from exact_tiled_attention_13_amd import tune
+
+    with open(tiles.DEFAULT_PATH) as fh:
+        doc = json.load(fh)
+    old = doc["entries"]
+    key = ("fwd", "bf16", 128)
+    fresh = [dict(e, choice=[1, -1]) for e in old if (e["op"], e["dtype"], e["D"]) == key]
+    assert fresh, "the packaged table has entries for the re-tuned key"
+    merged = tune.merge_only(old, fresh, key)
+    others = [e for e in old if (e["op"], e["dtype"], e["D"]) != key]
+    assert merged[: len(others)] == others
+    assert merged[len(others):] == fresh
+    assert len(merged) == len(old)
+    tiles.entries_from_json(dict(doc, entries=merged))
+    with pytest.raises(ValueError):
+        tune.merge_only(old, [dict(fresh[0], D=64)], key)
