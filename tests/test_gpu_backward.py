@@ -80,9 +80,10 @@ def test_small_shapes(D, causal, T):
     run(2, 4, 2, T, T, D, causal, seed=T)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("Tq,Tk", [(1, 200), (17, 300), (130, 129), (300, 17), (257, 513)])
-def test_bottom_right_causal(Tq, Tk):
-    run(1, 2, 1, Tq, Tk, 64, True, seed=Tq + Tk)
+def test_bottom_right_causal(Tq, Tk, D):
+    run(1, 2, 1, Tq, Tk, D, True, seed=Tq + Tk)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -91,14 +92,16 @@ def test_ragged_with_poison(D, causal):
     run(5, 4, 2, 300, 300, D, causal, lens=[1, 0, 300, 129, 64], seed=3, poison=True)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("G", [1, 4, 8])
-def test_gqa_groups(G):
-    run(2, 8, 8 // G, 200, 200, 128, True, seed=10 + G)
+def test_gqa_groups(G, D):
+    run(2, 8, 8 // G, 200, 200, D, True, seed=10 + G)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.5])
-def test_unusual_scales(scale):
-    run(1, 2, 2, 100, 100, 64, True, scale=scale, seed=7)
+def test_unusual_scales(scale, D):
+    run(1, 2, 2, 100, 100, D, True, scale=scale, seed=7)
 
 
 def elementwise(what, got, ref):
