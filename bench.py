@@ -61,7 +61,6 @@ CSRC = os.path.join(ROOT, "exact_tiled_attention_13_amd", "csrc")
 # kernel name (as rocprofv3 reports it, substring) -> sources it is built from
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["fwd_bf16.hip", "device_common.h", "launch.h"],
-    "bwd_prep_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
     "bwd_dq_kernel": ["bwd_bf16.hip", "device_common.h", "launch.h"],
     "bwd_dkdv": ["bwd_bf16.hip", "device_common.h", "launch.h"],   # bwd_dkdv_pair_kernel
     "fwd_f32_kernel": ["fwd_f32.hip", "device_common.h"],
@@ -298,10 +297,10 @@ def backward_errors(bw, n_rows):
 
 
 def backward_traffic(workload):
-    """Scaled HBM bytes per step of the three gradient kernels from the
+    """Scaled HBM bytes per step of the two gradient kernels from the
     committed counter summary, or None (see traffic_for)."""
     total = 0.0
-    for kn in ("bwd_prep_kernel", "bwd_dq_kernel", "bwd_dkdv"):
+    for kn in ("bwd_dq_kernel", "bwd_dkdv"):
         t = traffic_for(kn, workload)
         if t is None:
             return None
@@ -777,7 +776,7 @@ def backward_entry(torch, name, steps, warmup, calls, args):
              flops_per_step=bw["flops"],
              roofline=dict(bound="mfma", achieved=round(achieved, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                            frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                           traffic=backward_traffic(name), kernels="bwd_prep + bwd_dq + bwd_dkdv",
+                           traffic=backward_traffic(name), kernels="bwd_dq + bwd_dkdv",
                            kernel_ms=round(ev_ms, 5)))
     e["parity"] = backward_errors(bw, args.check_rows)
     del runner, bw

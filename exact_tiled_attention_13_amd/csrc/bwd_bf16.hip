@@ -9,15 +9,16 @@
 //   dV = P^T dO,   dP = dO V^T,   dS = P * (dP - Drow),
 //   dQ = scale dS K,   dK = scale dS^T Q     (GQA: dK, dV summed over the group)
 //
-// Three kernels:
-//   bwd_prep   per row: Drow = sum(dO * O) and Lc = LSE * log2(e) (+inf for
-//              rows that get no gradient: padding rows, rows without keys),
-//              so that every later weight is one exp2(c s - Lc).
+// Two kernels:
 //   bwd_dq     one workgroup per (batch, query head, 32*NW query rows), the
 //              forward's transposed frame (a lane owns a query row): key and
 //              value tiles stream through LDS; S^T = K Q^T and dP^T = V dO^T
 //              (Q and dO fragments in registers), dS^T elementwise, then
-//              dQ^T += K^T dS^T with K^T from transposing LDS reads.
+//              dQ^T += K^T dS^T with K^T from transposing LDS reads.  It
+//              also computes per row Drow = sum(dO * O) and Lc = LSE * log2(e)
+//              (+inf for rows that get no gradient: padding rows, rows
+//              without keys), so that every weight is one exp2(c s - Lc),
+//              and writes them to the workspace for bwd_dkdv_pair.
 //   bwd_dkdv_pair  one workgroup per (batch, KV head, 128 keys), a lane
 //              owns a key: the query heads of the group and their query
 //              tiles stream through LDS.  Each block of 32 keys is owned by
@@ -185,55 +186,15 @@ __device__ __forceinline__ void valid_lengths(const int32_t* kv_lens, int b, int
   }
 }
 
-// ---------------------------------------------------------------- bwd_prep
-// Drow = sum_d dO * O and Lc = LSE * log2(e) per query row; 8 lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const u16* __restrict__ O, const u16* __restrict__ dO,
-                                                       const float* __restrict__ LSE,
-                                                       const int32_t* __restrict__ kv_lens, float* __restrict__ Drow,
-                                                       float* __restrict__ Lc, int Hq, int Tq, int Tk, long long rows) {
-  const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
-  const int j = threadIdx.x & 7;
-  float acc = 0.f;
-  if (row < rows) {
-    constexpr int PER = D / 8 / 8;   // 16-byte loads per lane
-    const u32x4* po = reinterpret_cast<const u32x4*>(O + row * D) + j * PER;
-    const u32x4* pd = reinterpret_cast<const u32x4*>(dO + row * D) + j * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const u32x4 a = po[i], g = pd[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = __builtin_fmaf(__uint_as_float(a[e] << 16), __uint_as_float(g[e] << 16), acc);
-        acc = __builtin_fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(g[e] & 0xffff0000u), acc);
-      }
-    }
-  }
-  acc += __shfl_xor(acc, 1, 8);
-  acc += __shfl_xor(acc, 2, 8);
-  acc += __shfl_xor(acc, 4, 8);
-  if (row < rows && j == 0) {
-    const long long bh = row / Tq;
-    const int i = (int)(row - bh * Tq);
-    const int b = (int)(bh / Hq);
-    int Lq, Lk;
-    valid_lengths(kv_lens, b, Tq, Tk, Lq, Lk);
-    const float l = LSE[row];
-    const bool has = i < Lq && l != kNegInf;
-    Drow[row] = has ? acc : 0.f;
-    Lc[row] = has ? l * kLog2e : __builtin_huge_valf();
-  }
-}
-
 // ---------------------------------------------------------------- bwd_dq
 // (at most 256 registers: two waves per SIMD; left alone the compiler spends
 // AccVGPRs and runs one)
 template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
     const u16* __restrict__ Q, const u16* __restrict__ K, const u16* __restrict__ V, const u16* __restrict__ dO,
-    const float* __restrict__ Drow, const float* __restrict__ Lc, const int32_t* __restrict__ kv_lens,
-    u16* __restrict__ dQ, int B, int Hq, int Hkv, int Tq, int Tk, int nqt, float c, float scale, int negk,
-    int uorder) {
+    const u16* __restrict__ O, const float* __restrict__ LSE, float* __restrict__ Drow, float* __restrict__ Lc,
+    const int32_t* __restrict__ kv_lens, u16* __restrict__ dQ, int B, int Hq, int Hkv, int Tq, int Tk, int nqt,
+    float c, float scale, int negk, int uorder) {
   constexpr int BN = 32, NS = 4, KS = D / 16, DB = D / 32, BM = 32 * NW;
   constexpr int TILE = BN * D;
   constexpr int LOADS = TILE * 2 / 1024, PER = (LOADS + NW - 1) / NW, VM_PER_TILE = 2 * PER;
@@ -294,8 +255,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool rok = qrow < Tq;
   row_fragments<KS>(qf, Q + qbase * D, qrow, qrow < Lq, h, negk ? 0x80008000u : 0u);
   row_fragments<KS>(gf, dO + qbase * D, qrow, qrow < Lq, h, 0u);
-  const float lc = rok ? Lc[qbase + qrow] : __builtin_huge_valf();
-  const float dr = rok ? Drow[qbase + qrow] : 0.f;
+  // Drow = sum_d dO O and Lc = LSE log2(e) of this lane's row (each lane of
+  // the pair l, l ^ 32 holds half of the row's columns), kept for this
+  // kernel and written for bwd_dkdv, which runs after it: 0 and +inf for
+  // rows that get no gradient (padding rows, rows without keys)
+  float dr, lc;
+  {
+    bf16x8 of[KS];
+    row_fragments<KS>(of, O + qbase * D, qrow, qrow < Lq, h, 0u);
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 a = __builtin_bit_cast(u32x4, of[ks]), g = __builtin_bit_cast(u32x4, gf[ks]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        part = __builtin_fmaf(__uint_as_float(a[e] << 16), __uint_as_float(g[e] << 16), part);
+        part = __builtin_fmaf(__uint_as_float(a[e] & 0xffff0000u), __uint_as_float(g[e] & 0xffff0000u), part);
+      }
+    }
+    const float dsum = xhalf_sum(part);
+    const float l = rok ? LSE[qbase + qrow] : kNegInf;
+    const bool has = qrow < Lq && l != kNegInf;
+    dr = has ? dsum : 0.f;
+    lc = has ? l * kLog2e : __builtin_huge_valf();
+    if (rok && h == 0) {
+      Drow[qbase + qrow] = dr;
+      Lc[qbase + qrow] = lc;
+    }
+  }
 
   const TileOffsets<D> to(lane);
   f32x16 dq[DB];
@@ -710,20 +697,13 @@ hipError_t launch_d(const BwdArgs& a, hipStream_t st) {
     return ((a.B * a.Hkv) % 8 == 0 && grid >= 4LL * device_cu_count()) ? 1 : 0;
   };
   {
-    const long long grid = (rows + 31) / 32;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)grid), dim3(256), 0, st, (const u16*)a.o,
-                       (const u16*)a.dout, a.lse, a.kv_lens, Drow, Lc, a.Hq, a.Tq, a.Tk, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
     const int nqt = (a.Tq + 32 * kDqWaves - 1) / (32 * kDqWaves);
     const long long grid = (long long)nqt * a.B * a.Hq;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((bwd_dq_kernel<D, kDqWaves, CAUSAL>), dim3((unsigned)grid), dim3(64 * kDqWaves), 0, st,
-                       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, Drow, Lc, a.kv_lens,
-                       (u16*)a.dq, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, a.scale, negk, uorder(grid));
+                       (const u16*)a.q, (const u16*)a.k, (const u16*)a.v, (const u16*)a.dout, (const u16*)a.o, a.lse,
+                       Drow, Lc, a.kv_lens, (u16*)a.dq, a.B, a.Hq, a.Hkv, a.Tq, a.Tk, nqt, c, a.scale, negk,
+                       uorder(grid));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
