@@ -146,6 +146,18 @@ class Graphed:
             self.g.replay()
 
 
+def quiet_host(seconds=0.5):
+    """Pause after host-side math (the oracle, CPU baselines, input
+    generation) and before the GPU work of a measurement.  The CPU math
+    libraries' worker threads keep spinning for a while after a call, and
+    while they do they compete with the thread that submits each node of a
+    graph replay to the GPU (HIP launches a graph's kernels from the host):
+    a full run measured a 2.9 ms stall and gaps of tens of microseconds
+    between the nodes of one replay of the short gradient step, whose
+    kernels themselves ran at their usual durations."""
+    time.sleep(seconds)
+
+
 def time_steps(torch, runner, steps, warmup, fn):
     """`warmup` untimed eager calls, then exactly the steps of whole graph
     replays (a multiple of runner.calls, at least `steps`), bracketed by
@@ -714,6 +726,7 @@ def decode_errors(dec, n_seq=3):
 
 def prefill_entry(torch, name, steps, warmup, calls, args, headline=False):
     pre = setup_prefill(torch, name)
+    quiet_host()
     runner = Graphed(torch, pre["step"], calls)
     check_graph_replay(torch, runner, pre["step"], pre["out"])
     ev_ms, wall_ms, n = time_steps(torch, runner, steps, warmup, pre["step"])
@@ -743,6 +756,7 @@ def decode_entry(torch, name, steps, warmup, calls, args):
     paged = name == "decode-paged"
     dec = (setup_decode_paged(torch, args.page_size) if paged else
            setup_decode_fp8(torch) if name == "decode-fp8" else setup_decode(torch))
+    quiet_host()
     runner = Graphed(torch, dec["step"], calls)
     check_graph_replay(torch, runner, dec["step"], dec["out"])
     ev_ms, wall_ms, n = time_steps(torch, runner, steps, warmup, dec["step"])
@@ -766,6 +780,7 @@ def decode_entry(torch, name, steps, warmup, calls, args):
 
 def backward_entry(torch, name, steps, warmup, calls, args):
     bw = setup_backward(torch, name)
+    quiet_host()
     runner = Graphed(torch, bw["step"], calls)
     check_graph_replay(torch, runner, bw["step"], bw["out"])
     ev_ms, wall_ms, n = time_steps(torch, runner, steps, warmup, bw["step"])
