@@ -216,3 +216,40 @@ def test_natural_and_zigzag_orders(B, Hq, Hkv, nqt):
         for i in range(grid // 2):
             assert zig[i][2] + 1 + zig[i + grid // 2][2] + 1 == nqt + 1
             assert zig[i][:2] == zig[i + grid // 2][:2]
+
+
+def dkdv_order(uorder, id_, B, Hkv, nkt):
+    """Workgroup id -> (b, hk, kt) of the dK/dV kernel (bwd_dkdv_pair_kernel)."""
+    NU = B * Hkv
+    if uorder:
+        k = id_ >> 3
+        ul = k // nkt
+        kt = k - ul * nkt
+        u = (id_ & 7) + 8 * ul
+        b, hk = divmod(u, Hkv)
+    else:
+        kt, bh = divmod(id_, NU)
+        b, hk = divmod(bh, Hkv)
+    return b, hk, kt
+
+
+@pytest.mark.parametrize("B,Hkv,nkt", [(1, 32, 256), (2, 8, 16), (4, 2, 7), (8, 1, 3), (3, 5, 4)])
+def test_gradient_key_tile_orders(B, Hkv, nkt):
+    """The dK/dV kernel owns one (batch, KV head, key tile) per workgroup.
+    Both orders are bijections, key tiles run from the first (under a causal
+    mask the first key tiles are seen by the most queries); with a multiple
+    of 8 units the unit order keeps each unit on one XCD.  The dQ kernel
+    maps its ids like the prefill's natural and unit orders (checked
+    above)."""
+    grid = B * Hkv * nkt
+    for uorder in ([0, 1] if (B * Hkv) % 8 == 0 else [0]):
+        got = [dkdv_order(uorder, i, B, Hkv, nkt) for i in range(grid)]
+        assert len(set(got)) == grid
+        assert all(0 <= b < B and 0 <= hk < Hkv and 0 <= kt < nkt for b, hk, kt in got)
+        per_unit = {}
+        for i, (b, hk, kt) in enumerate(got):
+            per_unit.setdefault((b, hk), []).append((i, kt))
+        for v in per_unit.values():
+            assert [kt for _, kt in v] == sorted(kt for _, kt in v)
+            if uorder:
+                assert len({i & 7 for i, _ in v}) == 1
