@@ -151,3 +151,59 @@ def test_workspace_size_covers_every_slot():
         written, _ = split_side(lens, S_max, Hkv * ((Hq // Hkv + 15) // 16), 4 * 512)
         top = max(((b * Hq + hq) * NS + max(v)) for (b, hbk), v in written.items() for hq in range(Hq))
         assert top < B * Hq * NS
+
+
+def paged_geometry(num_pages, page_size, max_blocks, Hkv):
+    """The host's checks and derived sizes for the paged calls (api.cpp):
+    page shift, and S_max = max_blocks * page_size (lengths are clamped to it)."""
+    if page_size < 8 or page_size > 65536 or page_size & (page_size - 1):
+        return None
+    sh = page_size.bit_length() - 1
+    cap = max_blocks * page_size
+    if cap > 0x7FFFFFFF or num_pages * Hkv * page_size > (1 << 40):
+        return None
+    return sh, cap
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_paged_rows_stay_in_the_pool(seed):
+    """For every key of every item of a paged decode: the lane that holds
+    its page number is one of the wave's 64, the block-table entry read is
+    inside the table row (entries past it read as 0), the page is clamped
+    into the pool whatever the table holds, and the row's offset is inside
+    the pool.  Logical key j is row j % P of page block_table[b][j // P]."""
+    rng = random.Random(seed)
+    P = 1 << rng.randint(3, 11)
+    Hkv = rng.choice([1, 2, 8])
+    D = rng.choice([64, 128])
+    max_blocks = rng.randint(1, 3 * SPLIT_KEYS // P + 3)
+    num_pages = rng.randint(1, 40)
+    sh, S_max = paged_geometry(num_pages, P, max_blocks, Hkv)
+    B = rng.randint(1, 4)
+    table = [[rng.randint(-5, num_pages + 5) for _ in range(max_blocks)] for _ in range(B)]
+    lens = [rng.randint(-2, S_max + 50) for _ in range(B)]
+    pool = num_pages * Hkv * P * D
+    for b in range(B):
+        L = clamp(lens[b], 0, S_max)
+        ns = (L + SPLIT_KEYS - 1) // SPLIT_KEYS
+        for s in range(ns):
+            k0, k1 = s * SPLIT_KEYS, min(s * SPLIT_KEYS + SPLIT_KEYS, L)
+            # tile == 0: lane i loads the page number of block (k0 >> sh) + i
+            pvec = []
+            for lane in range(64):
+                blk = (k0 >> sh) + lane
+                p = table[b][blk] if blk < max_blocks else 0
+                pvec.append(clamp(p, 0, num_pages - 1))
+            for key in range(k0, k1):
+                src = (key >> sh) - (k0 >> sh)
+                assert 0 <= src < 64
+                assert (k0 >> sh) + src < max_blocks            # the entry that key's page came from
+                page = pvec[src]
+                for hkv in range(Hkv):
+                    off = (((page * Hkv + hkv) << sh) + (key & (P - 1))) * D
+                    assert 0 <= off and off + D <= pool
+                # the page is the table's when the entry is valid
+                e = table[b][key >> sh]
+                if 0 <= e < num_pages:
+                    assert page == e
+
