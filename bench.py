@@ -21,6 +21,7 @@ CPU baseline and max-abs errors against the float64 oracle on sampled rows:
   prefill_fp8   the long causal prefill on E4M3 Q, K, V
   backward      gradients of the causal prefill (10*D flops per unmasked
                 pair: the five products of the backward)
+  backward_long gradients of the long prefill (5 steps)
   single        the fp32 single-head workload (latency-bound; information)
 
 Steps are replayed from HIP graphs so that host launch overhead does not
@@ -318,6 +319,26 @@ def backward_traffic(workload):
             return None
         total += t
     return total
+
+
+def backward_mfma_busy(workload):
+    """Matrix-unit busy share of the two gradient kernels together: each
+    kernel's share from the committed counter summary, weighted by its
+    dispatch time there; None if either is missing or stale (see
+    mfma_busy_for)."""
+    path = os.path.join(PROFILES, "mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        data = json.load(fh)
+    num = den = 0.0
+    for kn in ("bwd_dq_kernel", "bwd_dkdv"):
+        e = data.get(f"{kn}/{workload}")
+        if not e or e.get("sources_sha256_16") != sources_hash(kn):
+            return None
+        num += e["mfma_busy"] * e["dispatch_seconds"]
+        den += e["dispatch_seconds"]
+    return round(num / den, 4)
 
 
 def cpu_baseline_backward(name, budget_s):
@@ -791,7 +812,8 @@ def backward_entry(torch, name, steps, warmup, calls, args):
              flops_per_step=bw["flops"],
              roofline=dict(bound="mfma", achieved=round(achieved, 3), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                            frac=round(achieved / PEAK_BF16_TFLOPS, 4),
-                           traffic=backward_traffic(name), kernels="bwd_dq + bwd_dkdv",
+                           traffic=backward_traffic(name), mfma_busy=backward_mfma_busy(name),
+                           kernels="bwd_dq + bwd_dkdv",
                            kernel_ms=round(ev_ms, 5)))
     e["parity"] = backward_errors(bw, args.check_rows)
     del runner, bw

@@ -207,3 +207,17 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_backward_busy_share_is_time_weighted(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench.backward_mfma_busy("long") is None
+    h = bench.sources_hash("bwd_dq_kernel")
+    data = {"bwd_dq_kernel/long": dict(sources_sha256_16=h, mfma_busy=0.6, dispatch_seconds=1.0),
+            "bwd_dkdv/long": dict(sources_sha256_16=h, mfma_busy=0.3, dispatch_seconds=2.0)}
+    json.dump(data, open(tmp_path / "mfma.json", "w"))
+    assert bench.backward_mfma_busy("long") == pytest.approx((0.6 * 1 + 0.3 * 2) / 3, abs=1e-4)
+    assert bench.backward_mfma_busy("causal") is None            # no entries for that workload
+    data["bwd_dkdv/long"]["sources_sha256_16"] = "0" * 16
+    json.dump(data, open(tmp_path / "mfma.json", "w"))
+    assert bench.backward_mfma_busy("long") is None              # one of the two is stale
