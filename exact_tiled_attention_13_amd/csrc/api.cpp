@@ -255,9 +255,8 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Tq <= 0 || Tk <= 0 || D <= 0 || Hq % Hkv != 0 || !std::isfinite(scale))
     return MIATTN_ERR_SHAPE;
   if (!supported_d(D) || dtype != MIATTN_BF16 || (causal != 0 && causal != 1)) return MIATTN_ERR_UNSUPPORTED;
-  // 128 query rows (dQ) and 128 keys (dK, dV) per workgroup, 32 rows per prep block
-  if ((long long)((Tq + 127) / 128) * B * Hq > 0x7fffffffLL || (long long)((Tk + 127) / 128) * B * Hkv > 0x7fffffffLL ||
-      ((long long)B * Hq * Tq + 31) / 32 > 0x7fffffffLL)
+  // 128 query rows (dQ) and 128 keys (dK, dV) per workgroup: each grid must fit a 1-D launch
+  if ((long long)((Tq + 127) / 128) * B * Hq > 0x7fffffffLL || (long long)((Tk + 127) / 128) * B * Hkv > 0x7fffffffLL)
     return MIATTN_ERR_SHAPE;
   const size_t need = attn_bwd_workspace_size(B, Hq, Tq);
   if (!workspace || workspace_bytes < need) return MIATTN_ERR_WORKSPACE;

@@ -147,6 +147,7 @@ def test_workspace_size(lib):
 @pytest.mark.parametrize("args,code", [
     (dict(q=0), -1), (dict(lse=0), -1), (dict(dout=0), -1), (dict(dq=0), -1), (dict(dv=0), -1), (dict(o=0), -1),
     (dict(B=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(scale=float("nan")), -2), (dict(Tk=0), -2),
+    (dict(B=65535, Hq=65535, Hkv=1, Tq=128), -2), (dict(B=65535, Hq=65535, Hkv=65535, Tk=128), -2),
     (dict(D=96), -3), (dict(dtype=0), -3), (dict(causal=3), -3),
     (dict(workspace=0), -4), (dict(workspace_bytes=10), -4),
     (dict(q=ODD4), -6), (dict(dout=ODD4), -6), (dict(dq=ODD4), -6), (dict(dk=ODD), -6), (dict(dv=ODD4), -6),
