@@ -1,4 +1,4 @@
-"""Masking in the prefill kernel, on the CPU.
+"""Masking in the prefill and dK/dV kernels, on the CPU.
 
 The prefill kernel (`fwd_tile` in csrc/fwd_bf16.hip) never evaluates the
 mask on every score.  A workgroup walks only the key tiles up to the last
@@ -12,7 +12,8 @@ key block kb holds key 32 kb + 8 (r >> 2) + 4 h + (r & 3)).  It checks that
 the (query, key) pairs that reach the softmax are exactly the pairs the
 mask allows, each once, over the three workgroup shapes and many lengths:
 key padding, padded query rows and bottom-right causal alignment
-("Implementing attention from scratch", *Masks* and *KV caching*).
+("Implementing attention from scratch", *Masks* and *KV caching*).  The
+same is checked for the dK/dV kernel's query steps (`dkdv_pairs`).
 """
 
 import random
@@ -98,3 +99,57 @@ def test_masks_random_lengths(seed):
     Lk = rng.randint(0, 700)
     Lq = Lk if rng.random() < 0.5 else rng.randint(0, 700)
     check(shape, causal, Lk, Lq)
+
+
+def dkdv_pairs(D, causal, Lk, Lq, G, kt):
+    """(query head in the group, query row, key) triples whose weights reach
+    dK/dV of key tile kt in `bwd_dkdv_pair_kernel` (csrc/bwd_bf16.hip): four
+    wave pairs of 32 keys each, query steps of 32 rows over the group's query
+    heads, a step skipped by the pair at D = 64 when none of its keys is
+    seen, masked when it crosses a boundary.  Accumulator element r of lane
+    32 h + r32 is query row q0 + 8 (r >> 2) + 4 h + (r & 3) against key
+    wkey0 + r32."""
+    NPAIR, BMQ = 4, 32
+    BNK = 32 * NPAIR
+    off = Lk - Lq
+    k0 = kt * BNK
+    qfirst = qend = 0
+    if k0 < Lk:
+        qfirst = max(0, k0 - off) if causal else 0
+        qend = Lq
+    nsteps_h = (qend - qfirst + BMQ - 1) // BMQ if qend > qfirst else 0
+    out = []
+    for pr in range(NPAIR):
+        wkey0 = k0 + 32 * pr
+        qwave_first = wkey0 - off if causal else 0
+        for sidx in range(G * nsteps_h):
+            g, j = divmod(sidx, nsteps_h)
+            q0 = qfirst + j * BMQ
+            if D == 64 and (wkey0 >= Lk or q0 + BMQ - 1 < qwave_first):
+                continue
+            needs_mask = (q0 + BMQ > Lq) or (wkey0 + 31 >= Lk) or (causal and wkey0 + 31 > q0 + off)
+            for h in range(2):
+                for r32 in range(32):
+                    key = wkey0 + r32
+                    for r in range(16):
+                        i = q0 + 8 * (r >> 2) + 4 * h + (r & 3)
+                        if needs_mask and not (i < Lq and key < Lk and (not causal or key <= i + off)):
+                            continue
+                        out.append((g, i, key))
+    return out
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Lk,Lq,G", [(1, 1, 1), (128, 128, 2), (129, 129, 1), (300, 300, 3), (300, 37, 1),
+                                     (37, 300, 2), (0, 5, 1), (5, 0, 1), (257, 1, 4)])
+def test_gradient_key_tile_masks(D, causal, Lk, Lq, G):
+    """Every allowed (query head, row, key) pair of a key tile reaches dK/dV
+    exactly once, and nothing else does."""
+    off = Lk - Lq
+    for kt in range(max(1, (Lk + 127) // 128) + 1):
+        got = dkdv_pairs(D, causal, Lk, Lq, G, kt)
+        want = [(g, i, j) for g in range(G) for i in range(Lq) for j in range(kt * 128, min(kt * 128 + 128, Lk))
+                if not causal or j <= i + off]
+        assert len(got) == len(set(got))
+        assert sorted(got) == sorted(want), (D, causal, Lk, Lq, G, kt)
