@@ -207,3 +207,28 @@ def test_paged_rows_stay_in_the_pool(seed):
                 if 0 <= e < num_pages:
                     assert page == e
 
+
+
+@pytest.mark.parametrize("BN", [32, 64])          # keys per tile: bf16 cache, E4M3 cache
+@pytest.mark.parametrize("L", [0, 1, 31, 32, 33, 511, 512, 513, 1000, 4097])
+def test_decode_tiles_cover_each_key_once(BN, L):
+    """Keys of a sequence reach the softmax once each: items of 512 keys
+    [k0, k1), tiles of BN keys from k0, and on a tile that passes k1 the
+    mask keeps key < k1.  Accumulator element r of lane 16 g + j in key
+    block kb is key kt + 16 kb + 4 g + r (v_mfma_f32_16x16, head column j)."""
+    got = []
+    ns = (L + SPLIT_KEYS - 1) // SPLIT_KEYS
+    for s in range(ns):
+        k0, k1 = s * SPLIT_KEYS, min(s * SPLIT_KEYS + SPLIT_KEYS, L)
+        ntiles = (k1 - k0 + BN - 1) // BN
+        for tile in range(ntiles):
+            kt = k0 + tile * BN
+            need_mask = kt + BN > k1
+            for kb in range(BN // 16):
+                for g in range(4):
+                    for r in range(4):
+                        key = kt + 16 * kb + 4 * g + r
+                        if need_mask and key >= k1:
+                            continue
+                        got.append(key)
+    assert sorted(got) == list(range(L))
