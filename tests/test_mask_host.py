@@ -159,8 +159,9 @@ def test_gradient_key_tile_masks(D, causal, Lk, Lq, G):
 @pytest.mark.parametrize("Lk,Lq", [(1, 1), (32, 32), (33, 33), (300, 300), (300, 37), (37, 300), (0, 5), (130, 0),
                                    (257, 1), (1000, 999)])
 def test_gradient_query_tile_masks(causal, Lk, Lq):
-    """The dQ kernel (`bwd_dq_kernel`) walks key tiles with the prefill's
-    rules: 128 query rows of 4 waves, 32-key tiles, one key block per tile
+    """The dQ kernel (`bwd_dq_kernel`) and the fp32 prefill (`fwd_f32_kernel`,
+    csrc/fwd_f32.hip) walk key tiles with the bf16 prefill's rules: 128
+    query rows of 4 waves, 32-key tiles, one key block per tile
     (accumulator key 8 (r >> 2) + 4 h + (r & 3)), the same kmax skip, kfull
     test and per-lane bound."""
     check((128, 32, 1, 4), causal, Lk, Lq)
